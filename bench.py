@@ -1,0 +1,301 @@
+"""Benchmark of the MoE grouped-GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the hot path over one batch of synthetic input that
+is already resident in HBM: routing (moegg_route) and the grouped GEMMs of
+the workload.  The default workload is the Mixtral-shaped first MoE GEMM
+(gate_up: T=4096 tokens, K=4096, N=28672, E=8, top-2, permute_x) with its
+backward: route + forward + dX + dW.  Other workloads:
+  fine    fine-grained down GEMM (T=8192, E=128, top-8, K=768, N=2048, Zipf
+          routing): route + forward (permute_y + fuse_mul_post) + dX + dW
+  decode  the same layer with T=64: route + forward (weights rotated over
+          several copies so every step reads them from HBM)
+  dual    two GEMM groups of different shapes in one launch
+  tiny    T=128, K=256, N=512, E=8, top-2: route + forward
+
+Prints ONE JSON line.  `value` is useful TFLOP/s over the whole step
+(useful FLOPs = 2 * sum_e m_e * N * K per GEMM, actual rows only);
+`roofline` describes the step's dominant kernel, timed with HIP events on
+the stream the kernels run on; `cpu_baseline` is the plain CPU oracle timed
+on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import token_routing_amd as mg  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+BLOCK_M = 128
+
+
+def _dev(t):
+    return t.to("cuda", non_blocking=False).contiguous()
+
+
+class Step:
+    """A workload's kernels, resident inputs and per-kernel accounting."""
+
+    def __init__(self, name):
+        self.name = name
+        self.kernels = []      # (label, fn, useful_flops, algorithmic_bytes)
+
+    def add(self, label, fn, flops, nbytes):
+        self.kernels.append((label, fn, float(flops), float(nbytes)))
+
+
+def _useful(m_sizes, N, K):
+    return 2.0 * float(np.sum(m_sizes)) * N * K
+
+
+def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1):
+    """route + forward (+ dX + dW) of one routed grouped GEMM."""
+    st = Step(wl.name)
+    E, N, K = wl.W.shape
+    S, T, topk = wl.S, wl.T, wl.topk
+    flags = wl.flags
+    ids = _dev(wl.ids)
+    X = _dev(wl.X)
+    Ws = [_dev(wl.W)]
+    for i in range(1, rotate):
+        Ws.append(Ws[0].clone())
+    weights = _dev(wl.weights.reshape(-1))
+    route_out = mg.moe_route(ids, E, BLOCK_M)
+    ws = torch.empty(max(mg.route_workspace_bytes(S, E), 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    m_sizes = route_out["m_sizes"].cpu().numpy()
+    nonempty = int((m_sizes > 0).sum())
+    Y = torch.empty(S, N, dtype=torch.bfloat16, device="cuda")
+    it = {"i": 0}
+
+    def route():
+        mg.moe_route(ids, E, BLOCK_M, out=route_out, workspace=ws)
+
+    def fwd():
+        W = Ws[it["i"] % len(Ws)]
+        it["i"] += 1
+        mg.grouped_gemm_fwd(X, W, route_out["m_sizes"], route_out["gather"], weights, topk, flags,
+                            Y=Y)
+
+    x_rows = T if (flags & synth.PERMUTE_X) else S
+    st.add("route", route, 0.0, S * 4 * 3 + E * 4 * 4)
+    st.add("fwd", fwd, _useful(m_sizes, N, K),
+           nonempty * N * K * 2 + x_rows * K * 2 + S * N * 2 + S * 4 * 2)
+    if with_bwd:
+        bwd_flags = flags & (synth.PERMUTE_X | synth.PERMUTE_Y)
+        dY = synth.normal_bf16((S, N), 0.01, synth.generator(dY_seed)).to("cuda")
+        dX = torch.empty(S, K, dtype=torch.bfloat16, device="cuda")
+        dW = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
+
+        def bwd_dx():
+            mg.grouped_gemm_dX(dY, Ws[0], route_out["m_sizes"], route_out["gather"], topk,
+                               bwd_flags, dX=dX)
+
+        def bwd_dw():
+            mg.grouped_gemm_dW(X, dY, route_out["m_sizes"], route_out["gather"], topk, bwd_flags,
+                               dW=dW)
+
+        st.add("dX", bwd_dx, _useful(m_sizes, N, K), S * N * 2 + nonempty * N * K * 2 + S * K * 2)
+        st.add("dW", bwd_dw, _useful(m_sizes, N, K), S * N * 2 + x_rows * K * 2 + E * N * K * 2)
+    st.m_sizes = m_sizes
+    st.inputs = wl
+    return st
+
+
+def build_dual_step(wl):
+    st = Step("dual")
+    groups = [(_dev(x), _dev(w)) for x, w in wl.groups]
+    outs = [torch.empty(x.shape[0], w.shape[1], dtype=torch.bfloat16, device="cuda")
+            for x, w in groups]
+    flops = sum(2.0 * x.shape[0] * x.shape[1] * w.shape[1] for x, w in groups)
+    nbytes = sum((x.numel() + w.numel() + x.shape[0] * w.shape[1]) * 2 for x, w in groups)
+    st.add("groups", lambda: mg.grouped_gemm_groups(groups, 0, outputs=outs), flops, nbytes)
+    st.inputs = wl
+    return st
+
+
+def make_step(name):
+    if name == "mixtral":
+        return build_layer_step(synth.mixtral(), dY_seed=2003)
+    if name == "fine":
+        return build_layer_step(synth.fine_bwd(), dY_seed=synth.SEEDS["fine_bwd_dy"])
+    if name == "fine_fwd":
+        return build_layer_step(synth.fine_down(), dY_seed=0, with_bwd=False)
+    if name == "decode":
+        return build_layer_step(synth.fine_decode(), dY_seed=0, with_bwd=False, rotate=4)
+    if name == "tiny":
+        return build_layer_step(synth.tiny(), dY_seed=0, with_bwd=False)
+    if name == "dual":
+        return build_dual_step(synth.dual())
+    raise SystemExit(f"unknown workload {name}")
+
+
+WORKLOAD_DESC = {
+    "mixtral": "Mixtral-shaped MoE gate_up grouped GEMM, T=4096 K=4096 N=28672 E=8 top-2, "
+               "permute_x; step = route + fwd + dX + dW",
+    "fine": "fine-grained MoE down grouped GEMM, T=8192 E=128 top-8 K=768 N=2048 Zipf(1.2); "
+            "step = route + fwd(permute_y+fuse_mul_post) + dX + dW",
+    "fine_fwd": "fine-grained MoE down grouped GEMM forward, T=8192 E=128 top-8 K=768 N=2048",
+    "decode": "fine-grained MoE down grouped GEMM decode slice, T=64 E=128 top-8 K=768 N=2048",
+    "dual": "asymmetric dual-expert GEMM: [512,1024]x[1024,2048] and [256,1024]x[1024,4096]",
+    "tiny": "tiny MoE grouped GEMM, T=128 K=256 N=512 E=8 top-2, permute_x",
+}
+
+
+def time_step(st, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for _, fn, _, _ in st.kernels:
+            fn()
+    torch.cuda.synchronize()
+    nk = len(st.kernels)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, (_, fn, _, _) in enumerate(st.kernels):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.zeros(nk)
+    total = 0.0
+    for s in range(steps):
+        for i in range(nk):
+            per[i] += ev[s][i].elapsed_time(ev[s][i + 1])
+        total += ev[s][0].elapsed_time(ev[s][nk])
+    return per / steps, total / steps, wall
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "route.hip", "common.h", "gemm_params.h"):
+        with open(os.path.join(ROOT, "token_routing_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, label):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{label}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(st, budget_s):
+    """The CPU oracle on a bounded sample of the workload (single thread)."""
+    import oracle
+
+    wl = st.inputs
+    t0 = time.perf_counter()
+    done_flops = 0.0
+    if st.name == "dual":
+        x, w = wl.groups[0]
+        rows = 64
+        oracle.dense_gemm_kn(synth.bits(x[:rows]), synth.bits(w))
+        done_flops = 2.0 * rows * x.shape[1] * w.shape[1]
+        sample = f"group 0, first {rows} rows"
+    else:
+        ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, BLOCK_M)
+        E, N, K = wl.W.shape
+        Xb, Wb = synth.bits(wl.X), synth.bits(wl.W)
+        rng = np.random.default_rng(0)
+        per_row = 2.0 * N * K
+        nrows = max(1, int(budget_s * 1.0e9 / per_row))   # ~1 GFLOP/s plain loops
+        rows = rng.choice(wl.S, size=min(nrows, wl.S), replace=False)
+        if wl.flags & synth.PERMUTE_Y:
+            rows = ref_route["gather"][rows]
+        oracle.grouped_gemm_fwd(Xb, Wb, ref_route["m_sizes"], ref_route["gather"],
+                                wl.weights.numpy().reshape(-1), wl.topk, wl.flags, rows=rows)
+        done_flops = per_row * len(rows)
+        sample = f"route (all {wl.S} slots) + forward of {len(rows)} random output rows x all {N} columns"
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_DESC))
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of CPU oracle work for the baseline (0 disables)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
+              "across GPUs", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    mg.load_library()
+
+    st = make_step(args.workload)
+    per, step_ms, wall = time_step(st, args.steps, args.warmup)
+    flops = sum(k[2] for k in st.kernels)
+    value = flops / (step_ms * 1e-3) / 1e12
+
+    breakdown = {}
+    dominant = max(range(len(st.kernels)), key=lambda i: per[i])
+    for i, (label, _, fl, nb) in enumerate(st.kernels):
+        t = per[i] * 1e-3
+        tf = fl / t / 1e12 if fl else 0.0
+        gbs = nb / t / 1e9
+        roof_t = max(fl / (PEAK_BF16_TFLOPS * 1e12), nb / (PEAK_HBM_GBS * 1e9))
+        breakdown[label] = {"ms": round(per[i], 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
+                            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "roofline_frac": round(roof_t / t, 4)}
+    label, _, fl, nb = st.kernels[dominant]
+    t = per[dominant] * 1e-3
+    mfma_bound = fl / (PEAK_BF16_TFLOPS * 1e12) >= nb / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved, peak, unit = fl / t / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = nb / t / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": "mfma" if mfma_bound else "hbm", "kernel": label,
+                "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(args.workload, label)}
+
+    cpu = cpu_baseline(st, args.cpu_budget) if args.cpu_budget > 0 else None
+    line = {
+        "metric": "MoE grouped-GEMM useful TFLOP/s (bf16) + % of MFMA/HBM roofline, fwd/dX/dW",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "desc": WORKLOAD_DESC[args.workload],
+                   "block_m_route": BLOCK_M},
+        "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

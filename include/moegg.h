@@ -1,0 +1,222 @@
+/*
+ * moegg.h -- MoE grouped GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmoegg.so: expert routing metadata, the forward grouped GEMM
+ * with its gather / scatter / gate-multiply fusions, its two backward
+ * GEMMs, and a launch of explicit GEMM groups of different shapes.
+ *
+ * Conventions shared by every entry point
+ *   T = num_tokens, k = topk, S = T * k routed slots; slot s = t * k + j is
+ *   the j-th expert choice of token t (row-major [T, k] order).
+ *   E = num_experts.  W is [E, N, K] row-major (K contiguous), the layout of
+ *   grouped_gemm_forward in unsloth grouped_gemm/interface.py.
+ *   bf16 tensors are row-major, 2 bytes per element, rows 16-byte aligned:
+ *   K and N must be multiples of 8 and base pointers 16-byte aligned.
+ *   Each input operand (X, dY, one expert's W, a group's x or w) must be
+ *   smaller than 2 GiB: the kernels address them with 32-bit offsets.
+ *   Index tensors are int32.  "sorted position" p indexes the expert-grouped
+ *   order: expert e owns positions [off[e], off[e] + m_sizes[e]).
+ *
+ * Ownership and ordering
+ *   Every pointer is a device pointer owned by the caller (unless stated as
+ *   a host pointer).  The library never allocates, frees or synchronises;
+ *   each call enqueues its kernels on `stream` (a hipStream_t; NULL is the
+ *   default stream) and returns.  Calls on one stream run in order.
+ *   Every element of every output is written by the call (the caller need
+ *   not clear outputs), except rows that belong to dropped slots.
+ *
+ * Errors
+ *   Host-checkable preconditions (the asserts of the pages' launchers)
+ *   return a status before anything is enqueued.  Data-dependent problems
+ *   found on the device (an expert id outside [0, E), m_sizes that are
+ *   negative or sum past S, a gather index outside [0, S)) are ORed as
+ *   MOEGG_DERR_* bits into *error_flags when that pointer is non-NULL; the
+ *   kernels skip the offending rows instead of faulting.  *error_flags is
+ *   sticky: the library never clears it.
+ */
+#ifndef MOEGG_H
+#define MOEGG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOEGG_OK = 0,
+    MOEGG_EINVAL = 1,       /* illegal flag combination or missing pointer       */
+    MOEGG_ESHAPE = 2,       /* non-positive, misaligned or inconsistent sizes     */
+    MOEGG_EUNSUPPORTED = 3, /* legal on the pages but not offered here            */
+    MOEGG_EWORKSPACE = 4,   /* workspace missing or smaller than required         */
+    MOEGG_EHIP = 5          /* a HIP launch or query failed                       */
+} moegg_status;
+
+/* Flags: the pages' fusion switches (grouped_gemm_forward arguments). */
+#define MOEGG_PERMUTE_X 1u     /* gather X rows from token order on load          */
+#define MOEGG_PERMUTE_Y 2u     /* scatter output rows back to slot order on store */
+#define MOEGG_FUSE_MUL_POST 4u /* multiply each output row by its gate weight     */
+#define MOEGG_DW_FP32_OUT 8u   /* dW only: write fp32 instead of bf16             */
+
+/* Device error bits ORed into *error_flags. */
+#define MOEGG_DERR_EXPERT_ID 1 /* a top-k expert id outside [0, E): slot dropped  */
+#define MOEGG_DERR_M_SIZES 2   /* m_sizes negative or summing past S: clipped     */
+#define MOEGG_DERR_GATHER 4    /* a gather index outside [0, S): row skipped      */
+
+#define MOEGG_MAX_EXPERTS 1024
+#define MOEGG_MAX_GROUPS 16
+
+/* Human-readable name of a status code (static string). */
+const char *moegg_status_string(moegg_status status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t moegg_version(void);
+
+/*
+ * Bytes of device workspace moegg_route needs for num_slots = T * k slots
+ * and num_experts experts (per-chunk expert counts).  0 for num_slots = 0.
+ */
+size_t moegg_route_workspace_bytes(int64_t num_slots, int32_t num_experts);
+
+/*
+ * moegg_route -- expert histogram, offsets and stable gather/scatter indices.
+ *
+ * Follows the routing metadata the pages consume: m_sizes ("tokens assigned
+ * to each expert", grouped_gemm_forward docstring, grouped_gemm/interface.py),
+ * expt_hist and its cumsum offsets, the block-padded layout of the ragged dw
+ * comment block, and GatherIndx / ScatterIndx ("dst_idx[src_idx] = arange")
+ * in triton_kernels/matmul_ogs.py.
+ *
+ *   topk_ids       [S] int32, slot order (the router's [T, k] ids).
+ *   m_sizes        out [E]   number of slots routed to each expert.
+ *   offsets        out [E+1] exclusive prefix sum of m_sizes.
+ *   padded_offsets out [E+1] the same with each count rounded up to a
+ *                  multiple of block_m; may be NULL.
+ *   tile_offsets   out [E+1] exclusive prefix sum of ceil(m_sizes/block_m);
+ *                  may be NULL.
+ *   gather_idx     out [S] slot held at sorted position p.  Within an expert,
+ *                  slots appear in ascending order (a stable sort).
+ *   scatter_idx    out [S] sorted position of slot s (the inverse of
+ *                  gather_idx); may be NULL.
+ *   workspace      device scratch of moegg_route_workspace_bytes(S, E) bytes,
+ *                  contents need no initialisation.
+ *
+ * A slot whose id is outside [0, E) is dropped: scatter_idx = -1, the
+ * positions it would have used stay at the end with gather_idx = -1, and
+ * MOEGG_DERR_EXPERT_ID is raised.  Results are bit-for-bit deterministic.
+ * Errors: ESHAPE if T < 0, k < 1, E < 1, E > MOEGG_MAX_EXPERTS or
+ * block_m < 1; EINVAL for a NULL required pointer; EWORKSPACE if
+ * workspace_bytes is too small.  T = 0 writes zero histograms and offsets.
+ */
+moegg_status moegg_route(const int32_t *topk_ids, int32_t num_tokens, int32_t topk,
+                         int32_t num_experts, int32_t block_m, int32_t *m_sizes,
+                         int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets,
+                         int32_t *gather_idx, int32_t *scatter_idx, void *workspace,
+                         size_t workspace_bytes, int32_t *error_flags, void *stream);
+
+/*
+ * moegg_grouped_gemm_fwd -- Y_e = X_e W_e^T for every expert, one launch.
+ *
+ * grouped_gemm_forward (grouped_gemm/interface.py) and the per-expert loop
+ * of matmul_ogs_torch (triton_kernels/matmul_ogs.py).  For sorted position p
+ * of expert e, with fp32 accumulation:
+ *   y[n] = sum_k X[src(p), k] * W[e, n, k]
+ *   src(p) = gather_idx[p] / topk with MOEGG_PERMUTE_X (X is [T, K], token
+ *            order), else p (X is [S, K], already in expert order);
+ *   MOEGG_FUSE_MUL_POST: y *= topk_weights[gather_idx[p]] (fp32 gate of the
+ *            slot, topk_weights is [S] in slot order);
+ *   stored as bf16 (round to nearest even) to row gather_idx[p] of Y with
+ *   MOEGG_PERMUTE_Y, else to row p.  Y is [S, N].
+ *
+ *   m_sizes     [E] device int32 rows per expert (moegg_route output); read
+ *               on the device, no host synchronisation.
+ *   gather_idx  [S] device int32; required with either permute flag.
+ *   error_flags optional device int32 (see Errors above).
+ *
+ * Errors: EINVAL if both permute flags are set, FUSE_MUL_POST without
+ * PERMUTE_Y, or a required pointer is NULL (gather_idx with a permute flag,
+ * topk_weights with FUSE_MUL_POST); ESHAPE for non-positive sizes, K or N
+ * not a multiple of 8, E > MOEGG_MAX_EXPERTS.  T = 0 is a no-op.
+ */
+moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t *m_sizes,
+                                    const int32_t *gather_idx, const float *topk_weights,
+                                    int32_t num_tokens, int32_t topk, int32_t num_experts,
+                                    int32_t N, int32_t K, uint32_t flags, void *Y,
+                                    int32_t *error_flags, void *stream);
+
+/*
+ * moegg_grouped_gemm_dX -- dX_e = dY_e W_e (reduction over N), one launch.
+ *
+ * grouped_gemm_dX (grouped_gemm/interface.py).  `flags` are the permute
+ * flags the forward used:
+ *   dY row     q(p) = gather_idx[p] if the forward used PERMUTE_Y (dY is in
+ *              slot order and is gathered on load), else p;
+ *   dX[., k]   = sum_n dY[q(p), n] * W[e, n, k]   (fp32 accumulation)
+ *   stored bf16 to row gather_idx[p] if the forward used PERMUTE_X (scatter
+ *   back to slot order), else row p.  dY is [S, N], dX is [S, K]; summing a
+ *   token's top-k rows is left to the caller.
+ * Errors: EINVAL for both permute flags or a missing gather_idx;
+ * EUNSUPPORTED for FUSE_MUL_POST (the pages forbid it in training);
+ * ESHAPE as for the forward.
+ */
+moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t *m_sizes,
+                                   const int32_t *gather_idx, int32_t num_tokens, int32_t topk,
+                                   int32_t num_experts, int32_t N, int32_t K, uint32_t flags,
+                                   void *dX, int32_t *error_flags, void *stream);
+
+/*
+ * moegg_grouped_gemm_dW -- dW_e = dY_e^T X_e, a reduction over each expert's
+ * own (ragged) number of rows, one launch.
+ *
+ * grouped_gemm_dW (grouped_gemm/interface.py) and the ragged-K
+ * "dw = matmul_ogs(x.T, dy)" formulation of triton_kernels/matmul_ogs.py:
+ *   dW[e, n, k] = sum_{p in e} dY[q(p), n] * X[r(p), k]  (fp32 accumulation)
+ *   r(p) = gather_idx[p] / topk with PERMUTE_X (X is [T, K]), else p
+ *   (X is [S, K]); q(p) = gather_idx[p] with PERMUTE_Y, else p.
+ * dW is [E, N, K], bf16, or fp32 with MOEGG_DW_FP32_OUT.  Experts with no
+ * rows get exact zeros.
+ * Errors: as for dX.
+ */
+moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t *m_sizes,
+                                   const int32_t *gather_idx, int32_t num_tokens, int32_t topk,
+                                   int32_t num_experts, int32_t N, int32_t K, uint32_t flags,
+                                   void *dW, int32_t *error_flags, void *stream);
+
+/*
+ * One GEMM group: y[m, n] = x[m, k] @ w, bf16 in, fp32 accumulation, bf16 out.
+ * w is [k, n] row-major (ldw >= n) when the call's trans_b is 0, as in
+ * asym_dual_gmm_separated (wall_x/fusions/backend.py), or [n, k] row-major
+ * (ldw >= k) when trans_b is 1.  Leading dimensions are in elements.
+ */
+typedef struct {
+    const void *x;
+    const void *w;
+    void *y;
+    int32_t m, n, k;
+    int32_t ldx, ldw, ldy;
+} moegg_group;
+
+/*
+ * moegg_grouped_gemm_groups -- several independent GEMMs of different shapes
+ * in one launch: the asymmetric dual-expert GEMM of asym_dual_gmm_separated
+ * ("output_expert0 = input_expert0 @ weight_expert0, output_expert1 =
+ * input_expert1 @ weight_expert1 ... as a single fused kernel call").
+ *
+ *   groups      HOST array of num_groups descriptors (copied at launch; it
+ *               may be freed when the call returns).  1 <= num_groups <=
+ *               MOEGG_MAX_GROUPS.  A group with m = 0 is skipped.
+ *   trans_b     0: w is [k, n]; 1: w is [n, k].  trans_a is not offered
+ *               (inputs are [m, k]).
+ * Errors: EINVAL for a NULL pointer or bad trans_b; ESHAPE for negative
+ * sizes, n, k, ldx, ldw, ldy not multiples of 8, or a leading dimension
+ * smaller than its row.
+ */
+moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_groups,
+                                       int32_t trans_b, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEGG_H */

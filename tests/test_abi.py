@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI: libmoegg.so loads, exports every function that
+include/moegg.h declares, and rejects bad arguments on the host with the
+documented status codes before any GPU call is made."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moegg.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import token_routing_amd as mg
+    if not os.path.exists(mg.LIB_PATH):
+        from token_routing_amd import build
+        build.build()
+    return mg.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moegg_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.moegg_version() >= 100
+    for code in range(6):
+        assert lib.moegg_status_string(code)
+
+
+def test_route_workspace_size(lib):
+    # one int32 count per (expert, 256-slot chunk)
+    assert lib.moegg_route_workspace_bytes(65536, 128) == 256 * 128 * 4
+    assert lib.moegg_route_workspace_bytes(1, 8) == 8 * 4
+    assert lib.moegg_route_workspace_bytes(0, 8) == 0
+
+
+EINVAL, ESHAPE, EUNSUP, EWS = 1, 2, 3, 4
+PX, PY, FM, F32 = 1, 2, 4, 8
+FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every case fails on the host
+
+
+@pytest.mark.parametrize("flags,want", [
+    (PX | PY, EINVAL),        # cannot permute both X and Y
+    (FM, EINVAL),             # fuse_mul_post requires permute_y
+    (PX | FM, EINVAL),
+    (16, EINVAL),             # unknown flag
+])
+def test_fwd_flag_checks(lib, flags, want):
+    st = lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, flags, FAKE,
+                                    None, None)
+    assert st == want
+
+
+def test_fwd_missing_pointers(lib):
+    # permute flag without gather indices; fuse_mul_post without weights
+    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, None, None, 10, 2, 8, 64, 64, PX, FAKE,
+                                      None, None) == EINVAL
+    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, None, 10, 2, 8, 64, 64, PY | FM,
+                                      FAKE, None, None) == EINVAL
+
+
+@pytest.mark.parametrize("T,k,E,N,K", [(-1, 2, 8, 64, 64), (10, 0, 8, 64, 64), (10, 2, 0, 64, 64),
+                                       (10, 2, 1025, 64, 64), (10, 2, 8, 60, 64),
+                                       (10, 2, 8, 64, 2), (10, 2, 8, 0, 64)])
+def test_fwd_shape_checks(lib, T, k, E, N, K):
+    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, T, k, E, N, K, 0, FAKE, None,
+                                      None) == ESHAPE
+
+
+def test_operand_size_limit(lib):
+    # one expert's W of 2 GiB does not fit 32-bit buffer offsets
+    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 32768, 32768, 0,
+                                      FAKE, None, None) == ESHAPE
+
+
+def test_backward_rejects_fuse_mul(lib):
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None,
+                                     None) == EUNSUP
+    assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None,
+                                     None) == EUNSUP
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, PX | PY, FAKE,
+                                     None, None) == EINVAL
+    assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, None, 10, 2, 8, 64, 64, PY, FAKE, None,
+                                     None) == EINVAL
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, F32, FAKE, None,
+                                     None) == EINVAL
+
+
+def test_route_checks(lib):
+    assert lib.moegg_route(FAKE, 10, 2, 8, 0, FAKE, FAKE, None, None, FAKE, None, FAKE, 1 << 20,
+                           None, None) == ESHAPE
+    assert lib.moegg_route(FAKE, 10, 2, 2000, 32, FAKE, FAKE, None, None, FAKE, None, FAKE,
+                           1 << 20, None, None) == ESHAPE
+    assert lib.moegg_route(FAKE, 10, 2, 8, 32, FAKE, FAKE, None, None, FAKE, None, FAKE, 4, None,
+                           None) == EWS
+    assert lib.moegg_route(FAKE, 10, 2, 8, 32, None, FAKE, None, None, FAKE, None, FAKE, 1 << 20,
+                           None, None) == EINVAL
+
+
+def test_groups_checks(lib):
+    import token_routing_amd as mg
+    g = (mg.MoeggGroup * 2)()
+    g[0] = mg.MoeggGroup(1 << 20, 1 << 20, 1 << 20, 16, 64, 64, 64, 64, 64)
+    g[1] = mg.MoeggGroup(1 << 20, 1 << 20, 1 << 20, 16, 60, 64, 64, 64, 64)  # n % 8 != 0
+    assert lib.moegg_grouped_gemm_groups(g, 2, 0, None) == ESHAPE
+    assert lib.moegg_grouped_gemm_groups(g, 1, 2, None) == EINVAL       # bad trans_b
+    assert lib.moegg_grouped_gemm_groups(g, 0, 0, None) == ESHAPE       # no groups
+    assert lib.moegg_grouped_gemm_groups(g, 17, 0, None) == ESHAPE
+    g[1] = mg.MoeggGroup(1 << 20, 1 << 20, 1 << 20, 16, 64, 64, 32, 64, 64)  # ldx < k
+    assert lib.moegg_grouped_gemm_groups(g, 2, 0, None) == ESHAPE

@@ -1,0 +1,366 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Routing outputs must match bit for bit.  bf16 GEMM outputs are compared with
+the oracle's fp32 results: relative Frobenius error <= 5e-3 and
+|y - ref| <= 3e-2 * max(1, |ref|) elementwise.  Small cases span several
+tiles with ragged tails, empty experts and every flag combination; the
+full-size workloads are checked on sampled rows and columns (all experts,
+tile boundaries, first and last rows) that the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._util import bf16_tolerance_ok
+
+pytestmark = pytest.mark.gpu
+
+PX, PY, FM = synth.PERMUTE_X, synth.PERMUTE_Y, synth.FUSE_MUL_POST
+
+
+@pytest.fixture(scope="module")
+def mg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_routing_amd as mg
+    mg.load_library()
+    return mg
+
+
+def _dev(t):
+    return t.to("cuda").contiguous()
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _assert_close(got_bf16, ref_f32, what):
+    got = got_bf16.float().cpu().numpy() if isinstance(got_bf16, torch.Tensor) else got_bf16
+    ok, info = bf16_tolerance_ok(got, ref_f32)
+    print(f"{what}: {info}", flush=True)
+    assert ok, (what, info)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+
+def _route_both(mg, ids_cpu, E, block_m):
+    ref = oracle.route(ids_cpu.numpy().reshape(-1), E, block_m)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = mg.moe_route(_dev(ids_cpu), E, block_m, error_flags=err)
+    torch.cuda.synchronize()
+    return ref, {k: _np(v) for k, v in out.items()}, int(err.item())
+
+
+ROUTE_CASES = [
+    ("tiny", lambda: synth.tiny().ids, 8, 32),
+    ("mixtral", lambda: synth.route_softmax_topk(4096, 8, 2, synth.generator(1003))[0], 8, 256),
+    ("fine_down", lambda: synth.fine_down().ids, 128, 256),
+    ("fine_decode", lambda: synth.fine_decode().ids, 128, 32),
+    ("E1024", lambda: torch.randint(0, 1024, (3001, 5), generator=synth.generator(9),
+                                    dtype=torch.int32), 1024, 64),
+    ("E1_odd", lambda: torch.zeros(777, 1, dtype=torch.int32), 1, 7),
+    ("E3_ragged", lambda: torch.randint(0, 3, (1000, 1), generator=synth.generator(3),
+                                        dtype=torch.int32), 3, 128),
+]
+
+
+@pytest.mark.parametrize("name,make,E,B", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_bit_exact(mg, name, make, E, B):
+    ids = make()
+    ref, got, err = _route_both(mg, ids, E, B)
+    assert err == 0
+    for k in ("m_sizes", "offsets", "padded_offsets", "tile_offsets", "gather", "scatter"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def test_route_deterministic(mg):
+    ids = _dev(synth.fine_down().ids)
+    first = {k: v.clone() for k, v in mg.moe_route(ids, 128, 256).items()}
+    for _ in range(10):
+        again = mg.moe_route(ids, 128, 256)
+        for k in first:
+            assert torch.equal(first[k], again[k]), k
+
+
+def test_route_drops_bad_ids(mg):
+    ids = torch.randint(0, 16, (513, 3), generator=synth.generator(5), dtype=torch.int32)
+    ids[7, 1] = -3
+    ids[400, 0] = 16
+    ids[512, 2] = 1 << 30
+    ref, got, err = _route_both(mg, ids, 16, 32)
+    assert err & 1
+    assert ref["dropped"] == 3
+    for k in ("m_sizes", "offsets", "gather", "scatter"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def test_route_empty(mg):
+    out = mg.moe_route(torch.zeros(0, 2, dtype=torch.int32, device="cuda"), 8, 32)
+    torch.cuda.synchronize()
+    assert _np(out["m_sizes"]).tolist() == [0] * 8
+    assert _np(out["offsets"]).tolist() == [0] * 9
+
+
+# ---------------------------------------------------------------------------
+# Forward
+# ---------------------------------------------------------------------------
+
+def _gpu_route(mg, wl, block_m=128):
+    return mg.moe_route(_dev(wl.ids), wl.E, block_m)
+
+
+def _fwd_case(mg, wl, flags, rows=None, cols=None):
+    r = _gpu_route(mg, wl)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    assert np.array_equal(_np(r["gather"]), ref_route["gather"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    Y = mg.grouped_gemm_fwd(_dev(wl.X), _dev(wl.W), r["m_sizes"], r["gather"],
+                            _dev(wl.weights.reshape(-1)), wl.topk, flags, error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = oracle.grouped_gemm_fwd(synth.bits(wl.X), synth.bits(wl.W), ref_route["m_sizes"],
+                                  ref_route["gather"], wl.weights.numpy().reshape(-1), wl.topk,
+                                  flags, rows=rows, cols=cols)
+    got = Y.float().cpu().numpy()
+    if rows is not None:
+        got = got[np.asarray(rows)]
+    if cols is not None:
+        got = got[:, np.asarray(cols)]
+    return got, ref, Y
+
+
+FWD_SMALL = [
+    # T, K, N, E, topk, seed, empty  -- ragged groups, tails in every dimension
+    (300, 320, 264, 5, 2, 1, (3,)),       # avg 120 rows/expert -> large-tile path
+    (700, 136, 520, 6, 3, 2, (0,)),       # K not a multiple of 64, N not of 256
+    (64, 256, 512, 16, 4, 3, (2, 9)),     # avg 16 rows -> small-tile path
+    (33, 64, 136, 40, 8, 4, (1, 5, 39)),  # tiny groups, many empty experts
+]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY, PY | FM], ids=["plain", "px", "py", "py_fm"])
+@pytest.mark.parametrize("case", FWD_SMALL, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in FWD_SMALL])
+def test_fwd_small(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty)
+    got, ref, _ = _fwd_case(mg, wl, flags)
+    _assert_close(got, ref, f"fwd {case} flags={flags}")
+
+
+def test_fwd_tiny_config(mg):
+    wl = synth.tiny()
+    got, ref, _ = _fwd_case(mg, wl, wl.flags)
+    _assert_close(got, ref, "fwd tiny")
+
+
+def test_fwd_decode_config(mg):
+    wl = synth.fine_decode()
+    got, ref, _ = _fwd_case(mg, wl, wl.flags)
+    _assert_close(got, ref, "fwd fine_decode")
+
+
+def _sample_rows(offsets, BM, extra, rng, S):
+    rows = set()
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        rows.update([lo, hi - 1, (lo + hi) // 2])
+        for b in range(lo + BM - 1, hi, BM):
+            rows.update([b, min(b + 1, hi - 1)])
+    rows.update(rng.integers(0, S, size=extra).tolist())
+    return np.array(sorted(rows))
+
+
+def _sample_cols(N, BN, extra, rng):
+    cols = {0, N - 1}
+    for b in range(BN - 1, N, BN * 7):
+        cols.update([b, min(b + 1, N - 1)])
+    cols.update(rng.integers(0, N, size=extra).tolist())
+    return np.array(sorted(cols), dtype=np.int32)
+
+
+def test_fwd_mixtral_sampled(mg):
+    wl = synth.mixtral()
+    rng = np.random.default_rng(0)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    rows_sorted = _sample_rows(ref_route["offsets"], 256, 16, rng, wl.S)
+    cols = _sample_cols(wl.N, 256, 48, rng)
+    got, ref, _ = _fwd_case(mg, wl, wl.flags, rows=rows_sorted, cols=cols)
+    _assert_close(got, ref, "fwd mixtral sampled")
+
+
+def test_fwd_fine_down_sampled(mg):
+    wl = synth.fine_down()
+    rng = np.random.default_rng(1)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    sorted_rows = _sample_rows(ref_route["offsets"], 256, 64, rng, wl.S)
+    out_rows = ref_route["gather"][sorted_rows]      # permute_y: output row = slot
+    cols = _sample_cols(wl.N, 256, 64, rng)
+    got, ref, _ = _fwd_case(mg, wl, wl.flags, rows=out_rows, cols=cols)
+    _assert_close(got, ref, "fwd fine_down sampled")
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+def _bwd_case(mg, wl, flags, dw_flags_extra=0, rows_dx=None, rows_dw=None, cols_dx=None,
+              cols_dw=None):
+    r = _gpu_route(mg, wl)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dY, W, X = _dev(wl.dY), _dev(wl.W), _dev(wl.X)
+    dX = mg.grouped_gemm_dX(dY, W, r["m_sizes"], r["gather"], wl.topk, flags, error_flags=err)
+    dW = mg.grouped_gemm_dW(X, dY, r["m_sizes"], r["gather"], wl.topk, flags | dw_flags_extra,
+                            error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    E, N, K = wl.W.shape
+    ref_dx = oracle.grouped_gemm_dX(synth.bits(wl.dY), synth.bits(wl.W), ref_route["m_sizes"],
+                                    ref_route["gather"], wl.topk, flags, rows=rows_dx, cols=cols_dx)
+    ref_dw = oracle.grouped_gemm_dW(synth.bits(wl.X), synth.bits(wl.dY), ref_route["m_sizes"],
+                                    ref_route["gather"], wl.topk, flags, E, rows=rows_dw,
+                                    cols=cols_dw)
+    got_dx = dX.float().cpu().numpy()
+    got_dw = dW.float().reshape(E * N, K).cpu().numpy()
+    if rows_dx is not None:
+        got_dx = got_dx[rows_dx]
+    if cols_dx is not None:
+        got_dx = got_dx[:, cols_dx]
+    if rows_dw is not None:
+        got_dw = got_dw[rows_dw]
+    if cols_dw is not None:
+        got_dw = got_dw[:, cols_dw]
+    return got_dx, ref_dx, got_dw, ref_dw, dW, ref_route
+
+
+BWD_SMALL = [
+    (300, 320, 264, 5, 2, 11, (3,)),
+    (700, 136, 520, 6, 3, 12, (0,)),
+    (33, 64, 136, 40, 8, 13, (1, 5, 39)),
+]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])
+@pytest.mark.parametrize("case", BWD_SMALL, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in BWD_SMALL])
+def test_bwd_small(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty, with_dy=True)
+    gdx, rdx, gdw, rdw, dW, _ = _bwd_case(mg, wl, flags)
+    _assert_close(gdx, rdx, f"dX {case} flags={flags}")
+    _assert_close(gdw, rdw, f"dW {case} flags={flags}")
+    for e in empty:
+        assert torch.count_nonzero(dW[e]).item() == 0
+
+
+def test_dw_fp32_out(mg):
+    wl = synth.random_case(300, 136, 264, 5, 2, PY, 21, empty=(2,), with_dy=True)
+    _, _, gdw, rdw, dW, _ = _bwd_case(mg, wl, PY, dw_flags_extra=mg.DW_FP32_OUT)
+    assert dW.dtype == torch.float32
+    ok, info = bf16_tolerance_ok(gdw, rdw, rel_fro_max=1e-5, max_elem=1e-4)
+    assert ok, info
+
+
+def test_bwd_fine_sampled(mg):
+    wl = synth.fine_bwd()
+    rng = np.random.default_rng(2)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    rows_dx = _sample_rows(ref_route["offsets"], 256, 32, rng, wl.S)
+    cols_dx = _sample_cols(wl.K, 256, 32, rng)
+    E, N, K = wl.W.shape
+    h = ref_route["m_sizes"]
+    experts = sorted(set([int(np.argmax(h)), int(np.argmin(np.where(h > 0, h, 10 ** 9)))]
+                         + rng.integers(0, E, 6).tolist() + np.nonzero(h == 0)[0][:2].tolist()))
+    rows_dw = np.array(sorted({e * N + n for e in experts for n in [0, 255, 256, N - 1]
+                               + rng.integers(0, N, 4).tolist()}))
+    cols_dw = _sample_cols(K, 256, 16, rng)
+    gdx, rdx, gdw, rdw, dW, _ = _bwd_case(mg, wl, wl.flags, rows_dx=rows_dx, rows_dw=rows_dw,
+                                           cols_dx=cols_dx, cols_dw=cols_dw)
+    _assert_close(gdx, rdx, "dX fine sampled")
+    _assert_close(gdw, rdw, "dW fine sampled")
+    for e in np.nonzero(h == 0)[0]:
+        assert torch.count_nonzero(dW[int(e)]).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# Explicit groups
+# ---------------------------------------------------------------------------
+
+def test_groups_dual_config(mg):
+    wl = synth.dual()
+    ys = mg.grouped_gemm_groups([(_dev(x), _dev(w)) for x, w in wl.groups], trans_b=0)
+    torch.cuda.synchronize()
+    for i, ((x, w), y) in enumerate(zip(wl.groups, ys)):
+        ref = oracle.dense_gemm_kn(synth.bits(x), synth.bits(w))
+        _assert_close(y, ref, f"dual group {i}")
+
+
+def test_groups_ragged_and_trans_b(mg):
+    g = synth.generator(77)
+    shapes = [(1, 64, 8), (130, 200, 264), (0, 64, 64), (257, 72, 136)]
+    xs = [synth.normal_bf16((m, k), 0.5, g) for m, k, n in shapes]
+    ws = [synth.normal_bf16((k, n), 0.5, g) for m, k, n in shapes]
+    ys = mg.grouped_gemm_groups([(_dev(x), _dev(w)) for x, w in zip(xs, ws)], trans_b=0)
+    ysT = mg.grouped_gemm_groups([(_dev(x), _dev(w.t().contiguous())) for x, w in zip(xs, ws)],
+                                 trans_b=1)
+    torch.cuda.synchronize()
+    for (m, k, n), x, w, y, yT in zip(shapes, xs, ws, ys, ysT):
+        if m == 0:
+            continue
+        ref = oracle.dense_gemm_kn(synth.bits(x), synth.bits(w))
+        _assert_close(y, ref, f"group {m}x{k}x{n}")
+        _assert_close(yT, ref, f"group trans_b {m}x{k}x{n}")
+
+
+# ---------------------------------------------------------------------------
+# Degenerate inputs and device-side error reporting
+# ---------------------------------------------------------------------------
+
+def test_zero_tokens_is_noop(mg):
+    W = torch.zeros(4, 64, 64, dtype=torch.bfloat16, device="cuda")
+    X = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    m = torch.zeros(4, dtype=torch.int32, device="cuda")
+    g = torch.zeros(0, dtype=torch.int32, device="cuda")
+    Y = mg.grouped_gemm_fwd(X, W, m, g, None, 2, PX)
+    assert Y.shape == (0, 64)
+    dW = mg.grouped_gemm_dW(X, torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda"), m, g, 2, 0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dW).item() == 0
+
+
+def test_bad_m_sizes_and_gather_are_flagged(mg):
+    wl = synth.random_case(64, 64, 64, 4, 2, PX, 31)
+    r = _gpu_route(mg, wl)
+    X, W = _dev(wl.X), _dev(wl.W)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bad_m = r["m_sizes"].clone()
+    bad_m[0] += 1000                      # sums past S: clipped, flagged
+    mg.grouped_gemm_fwd(X, W, bad_m, r["gather"], None, 2, PX, error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
+    err.zero_()
+    bad_g = r["gather"].clone()
+    bad_g[5] = 10 ** 6                    # outside [0, S): row skipped, flagged
+    mg.grouped_gemm_fwd(X, W, r["m_sizes"], bad_g, None, 2, PX, error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 4
+
+
+def test_host_validation_statuses(mg):
+    X = torch.zeros(8, 64, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(2, 64, 64, dtype=torch.bfloat16, device="cuda")
+    m = torch.tensor([4, 4], dtype=torch.int32, device="cuda")
+    g = torch.arange(8, dtype=torch.int32, device="cuda")
+    with pytest.raises(mg.MoeggError) as e:
+        mg.grouped_gemm_fwd(X, W, m, g, None, 1, PX | PY)
+    assert e.value.status == 1
+    with pytest.raises(mg.MoeggError) as e:
+        mg.grouped_gemm_dX(X, W, m, g, 1, FM)
+    assert e.value.status == 3

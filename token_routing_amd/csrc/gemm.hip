@@ -1,0 +1,792 @@
+// Persistent grouped-GEMM kernels for gfx950: forward (with permute_x,
+// permute_y and fuse_mul_post), dX, dW (ragged reduction per expert) and
+// explicit GEMM groups.
+//
+// The operations are those of grouped_gemm_forward / grouped_gemm_dX /
+// grouped_gemm_dW (unsloth grouped_gemm/interface.py), whose per-expert
+// meaning is the loop of matmul_ogs_torch (triton_kernels/matmul_ogs.py), and
+// of asym_dual_gmm_separated (wall_x/fusions/backend.py) for the groups.
+//
+// One engine serves all four.  A workgroup owns an output tile of BM x BN and
+// walks the reduction in stages of BK = 64 elements:
+//   * LDS holds both operands "reduction-contiguous": a tile row is the 64
+//     reduction elements (128 bytes) of one output row (A) or output column
+//     (B).  16-byte chunk c of row r lives at chunk c ^ (r & 7), so the eight
+//     lanes that read one chunk column of eight consecutive rows hit eight
+//     different bank groups.
+//   * v_mfma_f32_32x32x16_bf16 consumes the tile: lane l reads 8 reduction
+//     elements of row (l % 32) for A and of column (l % 32) for B.
+//   * Operands whose reduction index is contiguous in HBM (X and W in the
+//     forward, dY in dX) are copied 16 bytes per lane, eight lanes per
+//     128-byte row segment; gathered rows (permute_x, permute_y on load) are
+//     just per-row base pointers.
+//   * Operands whose reduction index runs across HBM rows (W in dX, dY and X
+//     in dW, a [K, N] weight in the groups) are read as 8 x 8 element blocks
+//     (eight 16-byte row segments), transposed in registers and written as
+//     eight 16-byte LDS chunks.
+//   * Two LDS stages: global loads for stage s+1 are in flight while the
+//     MFMAs consume stage s; one barrier per stage.
+//   * bf16 epilogue: fp32 accumulators (times the gate weight under
+//     fuse_mul_post) are rounded to bf16 into LDS, then written out as
+//     16-byte row segments, to row gather[p] under permute_y.
+//   * Persistent grid of (CUs x resident workgroups).  Every workgroup reads
+//     m_sizes and builds the tile map in LDS (no host synchronisation); tile
+//     t belongs to the expert whose tile range holds it.  Workgroup ids are
+//     remapped so that consecutive tiles run on the same XCD (own L2), and
+//     within an expert the M tiles of one N panel are consecutive, so the
+//     weight panel is fetched from HBM once per XCD.
+#include "common.h"
+
+#include "gemm_params.h"
+
+namespace moegg {
+
+constexpr int BK = 64;
+constexpr int kChunks = BK / 8;  // 16-byte chunks per LDS row
+
+__device__ __forceinline__ int lds_swz(int row, int chunk)
+{
+    return row * (BK * 2) + ((chunk ^ (row & 7)) << 4);
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NT = kWave * WM * WN;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(BM * BN * 2 <= LDS, "bf16 epilogue tile must fit in the operand buffers");
+};
+
+__device__ __forceinline__ uint32_t dw(const uint4 &v, int d)
+{
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// ---------------------------------------------------------------------------
+// Operand loaders
+// ---------------------------------------------------------------------------
+
+// Raw buffer resources: a 32-bit byte offset per lane and a uniform
+// descriptor.  An offset at or past num_records reads as zero, so a masked
+// row or column is the offset kOOB (operands are limited to 2 GiB each).
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// ROWS tile rows, reduction contiguous in HBM: thread t copies chunk t % 8 of
+// rows t / 8 + i * (NT / 8).  off[i] is that chunk's byte offset at k = 0
+// (kOOB: zero row).
+template <int ROWS, int NT>
+struct DirectLoader {
+    static constexpr int PASS = NT / kChunks;
+    static constexpr int RPT = (ROWS + PASS - 1) / PASS;
+    uint32_t off[RPT];
+    uint4 v[RPT];
+
+    __device__ __forceinline__ static int tile_row(int i) { return (threadIdx.x >> 3) + i * PASS; }
+
+    // row < 0 masks the row; row_bytes is the HBM row pitch.
+    __device__ __forceinline__ void set_row(int i, int64_t row, int64_t row_bytes)
+    {
+        off[i] = row < 0 ? kOOB : (uint32_t)(row * row_bytes) + (threadIdx.x & 7) * 16;
+    }
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int k0, int klen)
+    {
+        const bool kin = k0 + (int)(threadIdx.x & 7) * 8 < klen;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            v[i] = buf_load16(r, kin ? off[i] : kOOB, (uint32_t)k0 * 2);
+    }
+
+    __device__ __forceinline__ void store(char *lds) const
+    {
+        const int c = threadIdx.x & 7;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = tile_row(i);
+            if (ROWS % PASS == 0 || r < ROWS)
+                *reinterpret_cast<uint4 *>(lds + lds_swz(r, c)) = v[i];
+        }
+    }
+};
+
+// COLS tile rows whose reduction index runs across HBM rows.  The stage is
+// (BK / 8) x (COLS / 8) blocks of 8 x 8 elements; block b of thread t is
+// blk = t + b * NT with reduction block blk % 8 and column block blk / 8.
+// rowfn(red) gives the byte offset of the HBM row holding reduction index
+// red (kOOB: zeros).
+template <int COLS, int NT>
+struct TransLoader {
+    static constexpr int NBLK = (BK / 8) * (COLS / 8);
+    static constexpr int BPT = (NBLK + NT - 1) / NT;
+    uint4 v[BPT][8];
+
+    template <class RowFn>
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int red0, int col0, int ncols,
+                                         RowFn rowfn)
+    {
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+            const int blk = threadIdx.x + b * NT;
+            const int rb = blk & 7, cb = blk >> 3;
+            const int col = col0 + cb * 8;
+            const bool cin = (NBLK % NT == 0 || blk < NBLK) && col < ncols;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t ro = rowfn(red0 + rb * 8 + j);
+                v[b][j] = buf_load16(r, cin ? ro + (uint32_t)col * 2 : kOOB, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(char *lds) const
+    {
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+            const int blk = threadIdx.x + b * NT;
+            if (NBLK % NT != 0 && blk >= NBLK)
+                continue;
+            const int rb = blk & 7, cb = blk >> 3;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // column i of the 8 x 8 block: element i of rows 0..7
+                const int d = i >> 1;
+                uint32_t o[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = dw(v[b][2 * q], d), hi = dw(v[b][2 * q + 1], d);
+                    o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                   : ((lo & 0xffffu) | (hi << 16));
+                }
+                *reinterpret_cast<uint4 *>(lds + lds_swz(cb * 8 + i, rb)) =
+                    make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA stage and mainloop
+// ---------------------------------------------------------------------------
+
+template <class C>
+__device__ __forceinline__ void mma_stage(const char *As, const char *Bs,
+                                          f32x16_t (&acc)[C::FM][C::FN], int wm, int wn)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+        const int chunk = kk * 2 + half;
+        bf16x8_t a[C::FM], b[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            a[i] = *reinterpret_cast<const bf16x8_t *>(As + lds_swz(wm * C::TM + i * 32 + r, chunk));
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            b[j] = *reinterpret_cast<const bf16x8_t *>(Bs + lds_swz(wn * C::TN + j * 32 + r, chunk));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+}
+
+// load(s) issues the global loads of stage s into registers; store(As, Bs)
+// writes them to an LDS stage.  Ends with a barrier (LDS free for reuse).
+template <class C, class Load, class Store>
+__device__ __forceinline__ void mainloop(char *smem, int nsteps, f32x16_t (&acc)[C::FM][C::FN],
+                                         Load load, Store store)
+{
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    if (nsteps <= 0)
+        return;
+    load(0);
+    store(smem, smem + C::A_BYTES);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        char *cur = smem + (s & 1) * C::STAGE;
+        char *nxt = smem + ((s + 1) & 1) * C::STAGE;
+        const bool more = s + 1 < nsteps;
+        if (more)
+            load(s + 1);
+        mma_stage<C>(cur, cur + C::A_BYTES, acc, wm, wn);
+        if (more)
+            store(nxt, nxt + C::A_BYTES);
+        __syncthreads();
+    }
+}
+
+// Row and column of accumulator element r of 32x32 block (i, j) for this lane.
+template <class C>
+__device__ __forceinline__ int acc_row(int wm, int i, int r)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    return wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+template <class C>
+__device__ __forceinline__ int acc_col(int wn, int j)
+{
+    return wn * C::TN + j * 32 + (threadIdx.x & 31);
+}
+
+// bf16 epilogue through LDS.  s_dst[i]: destination row of tile row i (-1:
+// skip), s_scale: optional per-row factor.  Y is bf16 with leading dimension
+// ldy; tile column c maps to output column n0 + c (valid below ncols).
+template <class C>
+__device__ __forceinline__ void epilogue_bf16(char *smem, const f32x16_t (&acc)[C::FM][C::FN],
+                                              const int *s_dst, const float *s_scale, char *Y,
+                                              int64_t ldy, int n0, int ncols)
+{
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    uint16_t *tile = reinterpret_cast<uint16_t *>(smem);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = acc_row<C>(wm, i, r);
+                const int col = acc_col<C>(wn, j);
+                float v = acc[i][j][r];
+                if (s_scale)
+                    v *= s_scale[row];
+                tile[row * C::BN + col] = to_bf16(v);
+            }
+    __syncthreads();
+    constexpr int CPR = C::BN / 8;  // 16-byte chunks per tile row
+    for (int idx = threadIdx.x; idx < C::BM * CPR; idx += C::NT) {
+        const int row = idx / CPR, ch = idx % CPR;
+        const int dst = s_dst[row];
+        const int col = n0 + ch * 8;
+        if (dst >= 0 && col < ncols)
+            *reinterpret_cast<uint4 *>(Y + ((int64_t)dst * ldy + col) * 2) =
+                *reinterpret_cast<const uint4 *>(smem + (row * C::BN + ch * 8) * 2);
+    }
+    __syncthreads();
+}
+
+// fp32 epilogue straight from the accumulators (32 lanes = 128 contiguous bytes).
+template <class C>
+__device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[C::FM][C::FN], const int *s_dst,
+                                             float *Y, int64_t ldy, int n0, int ncols)
+{
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = acc_row<C>(wm, i, r);
+                const int col = n0 + acc_col<C>(wn, j);
+                const int dst = s_dst[row];
+                if (dst >= 0 && col < ncols)
+                    Y[(int64_t)dst * ldy + col] = acc[i][j][r];
+            }
+}
+
+// ---------------------------------------------------------------------------
+// Expert tables shared by the routed kernels
+// ---------------------------------------------------------------------------
+
+// s_roff[0..E]: expert row starts clipped to [0, S] (s_roff[E] = end);
+// s_tstart[0..E]: first tile of each expert for tiles_of(rows).  Flags
+// negative m_sizes and sums past S.
+template <class TilesOf>
+__device__ __forceinline__ int build_expert_tables(const int32_t *m_sizes, int E, int64_t S,
+                                                   int *s_roff, int *s_tstart, int *s_scratch,
+                                                   int32_t *err, TilesOf tiles_of)
+{
+    bool bad = false;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        const int m = m_sizes[e];
+        bad |= m < 0;
+        s_roff[e] = m < 0 ? 0 : m;
+    }
+    wave0_exclusive_scan(s_roff, E, &s_scratch[0]);
+    const int total = s_scratch[0];
+    if (threadIdx.x == 0) {
+        bad |= total > S || total < 0;
+        s_roff[E] = (int)min((int64_t)total, S);
+    }
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        s_roff[e] = (int)min((int64_t)s_roff[e], S);
+    if (bad)
+        raise_error(err, kErrMSizes);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        s_tstart[e] = tiles_of(s_roff[e + 1] - s_roff[e]);
+    wave0_exclusive_scan(s_tstart, E, &s_scratch[1]);
+    if (threadIdx.x == 0)
+        s_tstart[E] = s_scratch[1];
+    __syncthreads();
+    return s_tstart[E];
+}
+
+__device__ __forceinline__ int checked_gather(const int32_t *gather, int64_t p, int64_t S,
+                                              int32_t *err)
+{
+    const int g = gather[p];
+    if (g < 0 || g >= S) {
+        raise_error(err, kErrGather);
+        return -1;
+    }
+    return g;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
+{
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ int s_roff[kMaxExperts + 1];
+    __shared__ int s_tstart[kMaxExperts + 1];
+    __shared__ int s_src[C::BM];
+    __shared__ int s_dst[C::BM];
+    __shared__ float s_scale[C::BM];
+    __shared__ int s_scratch[2];
+
+    const bool px = a.flags & MOEGG_PERMUTE_X, py = a.flags & MOEGG_PERMUTE_Y;
+    const bool fm = a.flags & MOEGG_FUSE_MUL_POST;
+    const int ntn = (a.N + C::BN - 1) / C::BN;
+    const int total = build_expert_tables(a.m_sizes, a.E, a.S, s_roff, s_tstart, s_scratch, a.err,
+                                          [&](int m) { return (m + C::BM - 1) / C::BM * ntn; });
+    const int nsteps = (a.K + BK - 1) / BK;
+    const int64_t row_bytes = (int64_t)a.K * 2;
+    const int64_t x_rows = px ? a.S / a.topk : a.S;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, x_rows * row_bytes);
+
+    for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+        const int e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
+        const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1] - s_roff[e]);
+        const int p0base = __builtin_amdgcn_readfirstlane(s_roff[e]);
+        const int mtiles = (mc + C::BM - 1) / C::BM;
+        const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
+        const int mt = u % mtiles, nt = u / mtiles;
+        const int p0 = p0base + mt * C::BM;
+        const int rows = min(C::BM, mc - mt * C::BM);
+        const int n0 = nt * C::BN;
+
+        for (int i = threadIdx.x; i < C::BM; i += C::NT) {
+            int src = -1, dst = -1;
+            float scale = 1.0f;
+            if (i < rows) {
+                const int64_t p = p0 + i;
+                const int g = (px || py) ? checked_gather(a.gather, p, a.S, a.err) : (int)p;
+                if (g >= 0) {
+                    src = px ? g / a.topk : (int)p;
+                    dst = py ? g : (int)p;
+                    if (fm)
+                        scale = a.topk_w[g];
+                }
+            }
+            s_src[i] = src;
+            s_dst[i] = dst;
+            s_scale[i] = scale;
+        }
+        __syncthreads();
+
+        DirectLoader<C::BM, C::NT> la;
+        DirectLoader<C::BN, C::NT> lb;
+#pragma unroll
+        for (int i = 0; i < la.RPT; ++i) {
+            const int r = la.tile_row(i);
+            la.set_row(i, r < C::BM ? s_src[r] : -1, row_bytes);
+        }
+#pragma unroll
+        for (int i = 0; i < lb.RPT; ++i) {
+            const int r = lb.tile_row(i);
+            lb.set_row(i, (r < C::BN && n0 + r < a.N) ? n0 + r : -1, row_bytes);
+        }
+        const __amdgpu_buffer_rsrc_t wr =
+            make_rsrc(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
+
+        f32x16_t acc[C::FM][C::FN];
+        zero_acc<C>(acc);
+        mainloop<C>(
+            smem, nsteps, acc,
+            [&](int s) {
+                la.load(xr, s * BK, a.K);
+                lb.load(wr, s * BK, a.K);
+            },
+            [&](char *As, char *Bs) {
+                la.store(As);
+                lb.store(Bs);
+            });
+        epilogue_bf16<C>(smem, acc, s_dst, fm ? s_scale : nullptr, a.Y, a.N, n0, a.N);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dX = dY_e W_e  (reduction over N)
+// ---------------------------------------------------------------------------
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
+{
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ int s_roff[kMaxExperts + 1];
+    __shared__ int s_tstart[kMaxExperts + 1];
+    __shared__ int s_src[C::BM];
+    __shared__ int s_dst[C::BM];
+    __shared__ int s_scratch[2];
+
+    const bool px = a.flags & MOEGG_PERMUTE_X, py = a.flags & MOEGG_PERMUTE_Y;
+    const int ntk = (a.K + C::BN - 1) / C::BN;
+    const int total = build_expert_tables(a.m_sizes, a.E, a.S, s_roff, s_tstart, s_scratch, a.err,
+                                          [&](int m) { return (m + C::BM - 1) / C::BM * ntk; });
+    const int nsteps = (a.N + BK - 1) / BK;
+    const int64_t dy_row = (int64_t)a.N * 2, w_row = (int64_t)a.K * 2;
+    const __amdgpu_buffer_rsrc_t dyr = make_rsrc(a.dY, a.S * dy_row);
+
+    for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+        const int e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
+        const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1] - s_roff[e]);
+        const int p0base = __builtin_amdgcn_readfirstlane(s_roff[e]);
+        const int mtiles = (mc + C::BM - 1) / C::BM;
+        const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
+        const int mt = u % mtiles, kt = u / mtiles;
+        const int p0 = p0base + mt * C::BM;
+        const int rows = min(C::BM, mc - mt * C::BM);
+        const int k0 = kt * C::BN;
+
+        for (int i = threadIdx.x; i < C::BM; i += C::NT) {
+            int src = -1, dst = -1;
+            if (i < rows) {
+                const int64_t p = p0 + i;
+                const int g = (px || py) ? checked_gather(a.gather, p, a.S, a.err) : (int)p;
+                if (g >= 0) {
+                    src = py ? g : (int)p;
+                    dst = px ? g : (int)p;
+                }
+            }
+            s_src[i] = src;
+            s_dst[i] = dst;
+        }
+        __syncthreads();
+
+        DirectLoader<C::BM, C::NT> la;
+#pragma unroll
+        for (int i = 0; i < la.RPT; ++i) {
+            const int r = la.tile_row(i);
+            la.set_row(i, r < C::BM ? s_src[r] : -1, dy_row);
+        }
+        TransLoader<C::BN, C::NT> lb;
+        const __amdgpu_buffer_rsrc_t wr =
+            make_rsrc(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
+        const int N = a.N;
+        auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
+
+        f32x16_t acc[C::FM][C::FN];
+        zero_acc<C>(acc);
+        mainloop<C>(
+            smem, nsteps, acc,
+            [&](int s) {
+                la.load(dyr, s * BK, a.N);
+                lb.load(wr, s * BK, k0, a.K, wrowfn);
+            },
+            [&](char *As, char *Bs) {
+                la.store(As);
+                lb.store(Bs);
+            });
+        epilogue_bf16<C>(smem, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dW_e = dY_e^T X_e  (reduction over the expert's own rows)
+// ---------------------------------------------------------------------------
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
+{
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ int s_roff[kMaxExperts + 1];
+    __shared__ int s_tstart[kMaxExperts + 1];
+    __shared__ int s_order[kMaxExperts];
+    __shared__ int s_dst[C::BM];
+    __shared__ int s_scratch[2];
+
+    const bool px = a.flags & MOEGG_PERMUTE_X, py = a.flags & MOEGG_PERMUTE_Y;
+    const bool f32out = a.flags & MOEGG_DW_FP32_OUT;
+    const int ntn = (a.N + C::BM - 1) / C::BM, ntk = (a.K + C::BN - 1) / C::BN;
+    const int per_expert = ntn * ntk;
+    build_expert_tables(a.m_sizes, a.E, a.S, s_roff, s_tstart, s_scratch, a.err,
+                        [&](int) { return 0; });
+    // Longest experts first: the hot experts' long reductions start early.
+    for (int e = threadIdx.x; e < a.E; e += C::NT) {
+        const int m = s_roff[e + 1] - s_roff[e];
+        int rank = 0;
+        for (int f = 0; f < a.E; ++f) {
+            const int mf = s_roff[f + 1] - s_roff[f];
+            rank += (mf > m) || (mf == m && f < e);
+        }
+        s_order[rank] = e;
+    }
+    __syncthreads();
+    const int total = a.E * per_expert;
+    const int64_t dy_row = (int64_t)a.N * 2, x_row = (int64_t)a.K * 2;
+    const int64_t x_rows = px ? a.S / a.topk : a.S;
+    const __amdgpu_buffer_rsrc_t dyr = make_rsrc(a.dY, a.S * dy_row);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, x_rows * x_row);
+
+    for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+        const int e = __builtin_amdgcn_readfirstlane(s_order[t / per_expert]);
+        const int u = t % per_expert;
+        const int nt = u % ntn, kt = u / ntn;
+        const int n0 = nt * C::BM, k0 = kt * C::BN;
+        const int start = __builtin_amdgcn_readfirstlane(s_roff[e]);
+        const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1]) - start;
+
+        __syncthreads();
+        for (int i = threadIdx.x; i < C::BM; i += C::NT)
+            s_dst[i] = (n0 + i < a.N) ? e * a.N + n0 + i : -1;
+        __syncthreads();
+
+        const int64_t S = a.S;
+        const int32_t *gather = a.gather;
+        int32_t *err = a.err;
+        const int topk = a.topk;
+        auto dyrowfn = [=](int red) -> uint32_t {
+            if (red >= mc)
+                return kOOB;
+            const int64_t p = start + red;
+            const int q = py ? checked_gather(gather, p, S, err) : (int)p;
+            return q >= 0 ? (uint32_t)(q * dy_row) : kOOB;
+        };
+        auto xrowfn = [=](int red) -> uint32_t {
+            if (red >= mc)
+                return kOOB;
+            const int64_t p = start + red;
+            const int g = px ? checked_gather(gather, p, S, err) : (int)p;
+            return g >= 0 ? (uint32_t)((px ? g / topk : g) * x_row) : kOOB;
+        };
+        TransLoader<C::BM, C::NT> la;
+        TransLoader<C::BN, C::NT> lb;
+        f32x16_t acc[C::FM][C::FN];
+        zero_acc<C>(acc);
+        mainloop<C>(
+            smem, (mc + BK - 1) / BK, acc,
+            [&](int s) {
+                la.load(dyr, s * BK, n0, a.N, dyrowfn);
+                lb.load(xr, s * BK, k0, a.K, xrowfn);
+            },
+            [&](char *As, char *Bs) {
+                la.store(As);
+                lb.store(Bs);
+            });
+        if (f32out)
+            epilogue_f32<C>(acc, s_dst, reinterpret_cast<float *>(a.dW), a.K, k0, a.K);
+        else
+            epilogue_bf16<C>(smem, acc, s_dst, nullptr, a.dW, a.K, k0, a.K);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Explicit groups: y_g = x_g @ w_g
+// ---------------------------------------------------------------------------
+
+template <class C, bool TRANS_B>
+__global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
+{
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ int s_tstart[MOEGG_MAX_GROUPS + 1];
+    __shared__ int s_dst[C::BM];
+
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < a.num; ++i) {
+            s_tstart[i] = run;
+            run += ((a.g[i].m + C::BM - 1) / C::BM) * ((a.g[i].n + C::BN - 1) / C::BN);
+        }
+        s_tstart[a.num] = run;
+    }
+    __syncthreads();
+    const int total = s_tstart[a.num];
+
+    for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+        const int gi = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.num, t));
+        const moegg_group &g = a.g[gi];
+        const int mtiles = (g.m + C::BM - 1) / C::BM;
+        const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[gi]);
+        const int mt = u % mtiles, nt = u / mtiles;
+        const int m0 = mt * C::BM, n0 = nt * C::BN;
+
+        __syncthreads();
+        for (int i = threadIdx.x; i < C::BM; i += C::NT)
+            s_dst[i] = (m0 + i < g.m) ? m0 + i : -1;
+        __syncthreads();
+
+        const int64_t x_row = (int64_t)g.ldx * 2, w_row = (int64_t)g.ldw * 2;
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)g.m * x_row);
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(g.w, (int64_t)(TRANS_B ? g.n : g.k) * w_row);
+        DirectLoader<C::BM, C::NT> la;
+#pragma unroll
+        for (int i = 0; i < la.RPT; ++i) {
+            const int r = la.tile_row(i);
+            la.set_row(i, (r < C::BM && m0 + r < g.m) ? m0 + r : -1, x_row);
+        }
+        f32x16_t acc[C::FM][C::FN];
+        zero_acc<C>(acc);
+        const int nsteps = (g.k + BK - 1) / BK;
+        const int kk = g.k;
+        if constexpr (TRANS_B) {
+            DirectLoader<C::BN, C::NT> lb;
+#pragma unroll
+            for (int i = 0; i < lb.RPT; ++i) {
+                const int r = lb.tile_row(i);
+                lb.set_row(i, (r < C::BN && n0 + r < g.n) ? n0 + r : -1, w_row);
+            }
+            mainloop<C>(
+                smem, nsteps, acc,
+                [&](int s) {
+                    la.load(xr, s * BK, kk);
+                    lb.load(wr, s * BK, kk);
+                },
+                [&](char *As, char *Bs) {
+                    la.store(As);
+                    lb.store(Bs);
+                });
+        } else {
+            TransLoader<C::BN, C::NT> lb;
+            auto wrowfn = [=](int red) -> uint32_t {
+                return red < kk ? (uint32_t)(red * w_row) : kOOB;
+            };
+            const int n = g.n;
+            mainloop<C>(
+                smem, nsteps, acc,
+                [&](int s) {
+                    la.load(xr, s * BK, kk);
+                    lb.load(wr, s * BK, n0, n, wrowfn);
+                },
+                [&](char *As, char *Bs) {
+                    la.store(As);
+                    lb.store(Bs);
+                });
+        }
+        epilogue_bf16<C>(smem, acc, s_dst, nullptr, static_cast<char *>(g.y), g.ldy, n0, g.n);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+
+using BigCfg = Cfg<256, 256, 2, 4>;    // 512 threads, 128 KiB of operand LDS
+using SmallCfg = Cfg<32, 128, 1, 4>;   // few rows per expert: stream the weights
+using GroupCfg = Cfg<128, 128, 2, 2>;  // small explicit groups: more tiles
+
+static int64_t n_blocks_bound(int64_t rows, int E, int block)
+{
+    if (rows <= E)
+        return rows;
+    return (rows - E + 1 + block - 1) / block + E - 1;
+}
+
+template <class Kern>
+static int resident_blocks(Kern kernel, int threads)
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+        n = 1;
+    return n;
+}
+
+static int grid_for(int64_t tiles_bound, int cus, int resident)
+{
+    int64_t g = (int64_t)cus * resident;
+    if (tiles_bound < g)
+        g = tiles_bound;
+    return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream)
+{
+    const int64_t avg_rows = p.S / p.E;
+    if (avg_rows < 96) {
+        using C = SmallCfg;
+        const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.N + C::BN - 1) / C::BN);
+        static int res = resident_blocks(fwd_kernel<C>, C::NT);
+        hipLaunchKernelGGL(fwd_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    } else {
+        using C = BigCfg;
+        const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.N + C::BN - 1) / C::BN);
+        static int res = resident_blocks(fwd_kernel<C>, C::NT);
+        hipLaunchKernelGGL(fwd_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
+{
+    using C = BigCfg;
+    const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.K + C::BN - 1) / C::BN);
+    static int res = resident_blocks(dx_kernel<C>, C::NT);
+    hipLaunchKernelGGL(dx_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
+{
+    using C = BigCfg;
+    const int64_t tiles =
+        (int64_t)p.E * ((p.N + C::BM - 1) / C::BM) * ((p.K + C::BN - 1) / C::BN);
+    static int res = resident_blocks(dw_kernel<C>, C::NT);
+    hipLaunchKernelGGL(dw_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t groups_launch(const GroupsParams &p, int trans_b, int cus, hipStream_t stream)
+{
+    using C = GroupCfg;
+    int64_t tiles = 0;
+    for (int i = 0; i < p.num; ++i)
+        tiles += (int64_t)((p.g[i].m + C::BM - 1) / C::BM) * ((p.g[i].n + C::BN - 1) / C::BN);
+    if (trans_b) {
+        static int res = resident_blocks(groups_kernel<C, true>, C::NT);
+        hipLaunchKernelGGL((groups_kernel<C, true>), dim3(grid_for(tiles, cus, res)), dim3(C::NT),
+                           0, stream, p);
+    } else {
+        static int res = resident_blocks(groups_kernel<C, false>, C::NT);
+        hipLaunchKernelGGL((groups_kernel<C, false>), dim3(grid_for(tiles, cus, res)), dim3(C::NT),
+                           0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moegg

@@ -1,0 +1,68 @@
+// Kernel parameter blocks and host launchers of the grouped-GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moegg.h"
+
+namespace moegg {
+
+// Forward: Y = grouped X W_e^T with permute_x / permute_y / fuse_mul_post.
+struct FwdParams {
+    const char *X;
+    const char *W;
+    const int32_t *m_sizes;
+    const int32_t *gather;
+    const float *topk_w;
+    char *Y;
+    int32_t *err;
+    int64_t S;
+    int topk, E, N, K;
+    uint32_t flags;
+};
+
+// dX = grouped dY_e W_e.
+struct DxParams {
+    const char *dY;
+    const char *W;
+    const int32_t *m_sizes;
+    const int32_t *gather;
+    char *dX;
+    int32_t *err;
+    int64_t S;
+    int topk, E, N, K;
+    uint32_t flags;
+};
+
+// dW_e = dY_e^T X_e.
+struct DwParams {
+    const char *X;
+    const char *dY;
+    const int32_t *m_sizes;
+    const int32_t *gather;
+    char *dW;
+    int32_t *err;
+    int64_t S;
+    int topk, E, N, K;
+    uint32_t flags;
+};
+
+// Explicit groups (passed by value in the kernel arguments).
+struct GroupsParams {
+    moegg_group g[MOEGG_MAX_GROUPS];
+    int num;
+};
+
+hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream);
+hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream);
+hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream);
+hipError_t groups_launch(const GroupsParams &p, int trans_b, int cus, hipStream_t stream);
+
+int64_t route_chunks(int64_t S);
+hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32_t *m_sizes,
+                        int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets,
+                        int32_t *gather, int32_t *scatter, int32_t *counts, int32_t *err,
+                        hipStream_t stream);
+
+}  // namespace moegg

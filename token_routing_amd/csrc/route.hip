@@ -1,0 +1,225 @@
+// Routing metadata on the GPU: expert histogram, offsets (plain, padded,
+// tile) and the stable gather / scatter indices of the expert-grouped order.
+//
+// What is computed is the metadata the pages' grouped GEMMs consume: m_sizes
+// and "slicing gather_indices by cumsum of m_sizes" (grouped_gemm_forward
+// docstring, unsloth grouped_gemm/interface.py), expt_hist with its cumsum
+// offsets and block-padded offsets, and the inverse index pair of
+// GatherIndx / ScatterIndx (triton_kernels/matmul_ogs.py).
+//
+// Design (three launches on the caller's stream):
+//   1. route_count: every wave owns kSlotsPerWave consecutive slots (a
+//      "chunk") and counts them per expert.  Lanes holding the same expert id
+//      find each other with one wave ballot per id bit; the lowest such lane
+//      adds the group's popcount to a wave-private LDS histogram, so there is
+//      one LDS update per (expert, 64 slots) instead of one per slot.  Counts
+//      go to workspace as counts[e][chunk] (expert-major).
+//   2. route_scan (one workgroup): each wave scans whole experts' chunk rows
+//      with wave shuffles, turning counts[e][c] into the number of expert-e
+//      slots in chunks before c; then wave 0 scans the per-expert totals into
+//      offsets, padded offsets and tile offsets.
+//   3. route_scatter: each wave starts a per-expert cursor at
+//      offsets[e] + counts[e][chunk] and walks its chunk 64 slots at a time;
+//      a slot's position is its cursor plus the number of lower lanes with
+//      the same expert.  Chunks are in slot order and lanes are in slot
+//      order, so the result is the stable counting sort, bit for bit.
+#include "common.h"
+
+#include "gemm_params.h"
+
+namespace moegg {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / kWave;
+constexpr int kSlotsPerWave = 256;
+constexpr int kScanThreads = 1024;
+
+// Lanes (of the active, valid ones) that hold the same id as this lane.
+__device__ __forceinline__ uint64_t same_id_lanes(int id, bool valid, int nbits)
+{
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t on = __ballot(valid && bit);
+        m &= bit ? on : ~on;
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint64_t lanes_below()
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t *__restrict__ ids,
+                                                             int64_t S, int E, int nbits,
+                                                             int nchunks, int32_t *counts,
+                                                             int32_t *err)
+{
+    __shared__ int hist[kRouteWaves][kMaxExperts];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int chunk = blockIdx.x * kRouteWaves + wave;
+    for (int e = lane; e < E; e += kWave)
+        hist[wave][e] = 0;
+    __syncthreads();
+    bool dropped = false;
+    const int64_t base = (int64_t)chunk * kSlotsPerWave;
+    for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
+        const int64_t s = base + step * kWave + lane;
+        const bool in = chunk < nchunks && s < S;
+        const int id = in ? ids[s] : -1;
+        const bool valid = in && id >= 0 && id < E;
+        dropped |= in && !valid;
+        const uint64_t peers = same_id_lanes(id, valid, nbits);
+        if (valid && (peers & lanes_below()) == 0)
+            atomicAdd(&hist[wave][id], __popcll(peers));
+    }
+    __syncthreads();
+    if (chunk < nchunks)
+        for (int e = lane; e < E; e += kWave)
+            counts[(int64_t)e * nchunks + chunk] = hist[wave][e];
+    if (dropped)
+        raise_error(err, kErrExpertId);
+}
+
+__global__ __launch_bounds__(kScanThreads) void route_scan(int32_t *counts, int nchunks, int E,
+                                                           int block_m, int64_t S,
+                                                           int32_t *m_sizes, int32_t *offsets,
+                                                           int32_t *padded_offsets,
+                                                           int32_t *tile_offsets,
+                                                           int32_t *gather)
+{
+    __shared__ int tot[kMaxExperts];
+    __shared__ int off[kMaxExperts];
+    __shared__ int poff[kMaxExperts];
+    __shared__ int toff[kMaxExperts];
+    __shared__ int totals[3];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int kWaves = kScanThreads / kWave;
+    for (int e = wave; e < E; e += kWaves) {
+        int32_t *row = counts + (int64_t)e * nchunks;
+        int carry = 0;
+        for (int c0 = 0; c0 < nchunks; c0 += kWave) {
+            const int c = c0 + lane;
+            const int v = c < nchunks ? row[c] : 0;
+            int incl = v;
+            for (int d = 1; d < kWave; d <<= 1) {
+                int u = __shfl_up(incl, d, kWave);
+                if (lane >= d)
+                    incl += u;
+            }
+            if (c < nchunks)
+                row[c] = carry + incl - v;
+            carry += __shfl(incl, kWave - 1, kWave);
+        }
+        if (lane == 0)
+            tot[e] = carry;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kScanThreads) {
+        const int tiles = (tot[e] + block_m - 1) / block_m;
+        off[e] = tot[e];
+        poff[e] = tiles * block_m;
+        toff[e] = tiles;
+    }
+    wave0_exclusive_scan(off, E, &totals[0]);
+    wave0_exclusive_scan(poff, E, &totals[1]);
+    wave0_exclusive_scan(toff, E, &totals[2]);
+    for (int e = threadIdx.x; e < E; e += kScanThreads) {
+        m_sizes[e] = tot[e];
+        offsets[e] = off[e];
+        if (padded_offsets)
+            padded_offsets[e] = poff[e];
+        if (tile_offsets)
+            tile_offsets[e] = toff[e];
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = totals[0];
+        if (padded_offsets)
+            padded_offsets[E] = totals[1];
+        if (tile_offsets)
+            tile_offsets[E] = totals[2];
+    }
+    // Positions left over by dropped slots hold -1.
+    for (int64_t p = totals[0] + threadIdx.x; p < S; p += kScanThreads)
+        gather[p] = -1;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_scatter(const int32_t *__restrict__ ids,
+                                                               int64_t S, int E, int nbits,
+                                                               int nchunks,
+                                                               const int32_t *__restrict__ counts,
+                                                               const int32_t *__restrict__ offsets,
+                                                               int32_t *gather, int32_t *scatter)
+{
+    __shared__ int cursor[kRouteWaves][kMaxExperts];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int chunk = blockIdx.x * kRouteWaves + wave;
+    if (chunk < nchunks)
+        for (int e = lane; e < E; e += kWave)
+            cursor[wave][e] = offsets[e] + counts[(int64_t)e * nchunks + chunk];
+    __syncthreads();
+    const int64_t base = (int64_t)chunk * kSlotsPerWave;
+    for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
+        const int64_t s = base + step * kWave + lane;
+        const bool in = chunk < nchunks && s < S;
+        const int id = in ? ids[s] : -1;
+        const bool valid = in && id >= 0 && id < E;
+        const uint64_t peers = same_id_lanes(id, valid, nbits);
+        const uint64_t below = peers & lanes_below();
+        // All lanes read their cursor before any group leader advances it.
+        const int start = valid ? cursor[wave][id] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            const int pos = start + __popcll(below);
+            gather[pos] = (int32_t)s;
+            if (scatter)
+                scatter[s] = pos;
+            if (below == 0)
+                cursor[wave][id] = start + __popcll(peers);
+        } else if (in && scatter) {
+            scatter[s] = -1;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+static int bits_for(int E)
+{
+    int b = 0;
+    while ((1 << b) < E)
+        ++b;
+    return b;
+}
+
+int64_t route_chunks(int64_t S)
+{
+    return (S + kSlotsPerWave - 1) / kSlotsPerWave;
+}
+
+hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32_t *m_sizes,
+                        int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets,
+                        int32_t *gather, int32_t *scatter, int32_t *counts, int32_t *err,
+                        hipStream_t stream)
+{
+    const int nchunks = (int)route_chunks(S);
+    const int nbits = bits_for(E);
+    const int blocks = (nchunks + kRouteWaves - 1) / kRouteWaves;
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(route_count, dim3(blocks), dim3(kRouteThreads), 0, stream, ids, S, E,
+                           nbits, nchunks, counts, err);
+    }
+    hipLaunchKernelGGL(route_scan, dim3(1), dim3(kScanThreads), 0, stream, counts, nchunks, E,
+                       block_m, S, m_sizes, offsets, padded_offsets, tile_offsets, gather);
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(route_scatter, dim3(blocks), dim3(kRouteThreads), 0, stream, ids, S, E,
+                           nbits, nchunks, counts, offsets, gather, scatter);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moegg

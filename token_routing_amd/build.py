@@ -35,9 +35,9 @@ FLAGS = [
 SOURCES = ["route.hip", "gemm.hip", "api.hip"]
 
 
-def _compile(src: str, report: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, report: bool, defines=(), build_dir=BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if report:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,14 +49,15 @@ def _compile(src: str, report: bool) -> str:
     return obj
 
 
-def build(report: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(report: bool = False, defines=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile and link; `defines` are extra -D settings (tile-shape macros)."""
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, report), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, report, defines, build_dir), SOURCES))
+    tmp = out + ".tmp"
     subprocess.check_call([HIPCC, "-shared", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -35,6 +35,8 @@
 //     remapped so that consecutive tiles run on the same XCD (own L2), and
 //     within an expert the M tiles of one N panel are consecutive, so the
 //     weight panel is fetched from HBM once per XCD.
+#include <type_traits>
+
 #include "common.h"
 
 #include "gemm_params.h"
@@ -59,7 +61,6 @@ struct Cfg {
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int LDS = 2 * STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
-    static_assert(BM * BN * 2 <= LDS, "bf16 epilogue tile must fit in the operand buffers");
 };
 
 __device__ __forceinline__ uint32_t dw(const uint4 &v, int d)
@@ -93,7 +94,8 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 template <int ROWS, int NT>
 struct DirectLoader {
     static constexpr int PASS = NT / kChunks;
-    static constexpr int RPT = (ROWS + PASS - 1) / PASS;
+    static constexpr int RPT = ROWS / PASS;
+    static_assert(ROWS % PASS == 0, "loader covers whole passes");
     uint32_t off[RPT];
     uint4 v[RPT];
 
@@ -105,7 +107,7 @@ struct DirectLoader {
         off[i] = row < 0 ? kOOB : (uint32_t)(row * row_bytes) + (threadIdx.x & 7) * 16;
     }
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int k0, int klen)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char *, int k0, int klen)
     {
         const bool kin = k0 + (int)(threadIdx.x & 7) * 8 < klen;
 #pragma unroll
@@ -118,12 +120,60 @@ struct DirectLoader {
         const int c = threadIdx.x & 7;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int r = tile_row(i);
-            if (ROWS % PASS == 0 || r < ROWS)
-                *reinterpret_cast<uint4 *>(lds + lds_swz(r, c)) = v[i];
+            *reinterpret_cast<uint4 *>(lds + lds_swz(tile_row(i), c)) = v[i];
         }
     }
 };
+
+// ROWS tile rows, reduction contiguous in HBM, copied HBM -> LDS without
+// passing through registers (buffer_load_dwordx4 ... lds).  Lane l of a wave
+// writes LDS bytes [16 l, 16 l + 16) of the wave's 1 KiB window, i.e. physical
+// chunk l % 8 of window row l / 8; to land in the swizzled layout it fetches
+// logical chunk (l % 8) ^ (row % 8) = (l % 8) ^ (l / 8).  Wave w, pass i
+// fills rows 8 w + i * (NT / 8) .. + 7, so the eight lanes of a row still read
+// one whole 128-byte row segment.
+template <int ROWS, int NT>
+struct DmaLoader {
+    static constexpr int PASS = NT / kChunks;
+    static constexpr int RPT = ROWS / PASS;
+    static_assert(ROWS % PASS == 0, "DMA loader covers whole passes");
+    uint32_t off[RPT];
+
+    __device__ __forceinline__ static int tile_row(int i) { return (threadIdx.x >> 3) + i * PASS; }
+    __device__ __forceinline__ static int chunk()
+    {
+        const int l = threadIdx.x & (kWave - 1);
+        return (l & 7) ^ (l >> 3);
+    }
+
+    __device__ __forceinline__ void set_row(int i, int64_t row, int64_t row_bytes)
+    {
+        off[i] = row < 0 ? kOOB : (uint32_t)(row * row_bytes) + chunk() * 16;
+    }
+
+    __device__ __forceinline__ void store(char *) const {}
+
+    // Enqueue the copies of reduction stage k0 into the LDS stage `lds`.
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char *lds, int k0, int klen) const
+    {
+        const bool kin = k0 + chunk() * 8 < klen;
+        const int wave_row = (threadIdx.x / kWave) * 8;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            char *dst = lds + (i * PASS + wave_row) * (BK * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void *)dst, 16, kin ? off[i] : kOOB,
+                (uint32_t)k0 * 2, 0, 0);
+        }
+    }
+};
+
+// Wait until this wave's outstanding vector-memory operations (including
+// HBM -> LDS copies) have completed: s_waitcnt vmcnt(0), other counters free.
+__device__ __forceinline__ void wait_vmem()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 // COLS tile rows whose reduction index runs across HBM rows.  The stage is
 // (BK / 8) x (COLS / 8) blocks of 8 x 8 elements; block b of thread t is
@@ -184,6 +234,37 @@ struct TransLoader {
 // MFMA stage and mainloop
 // ---------------------------------------------------------------------------
 
+// All MFMA operands of one LDS stage, read into registers: lane l holds 8
+// reduction elements of tile row (l % 32) of each 32-row block, for the four
+// 16-deep MFMA steps of the stage.
+template <class C>
+struct StageFrags {
+    bf16x8_t a[BK / 16][C::FM];
+    bf16x8_t b[BK / 16][C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(const char *As, const char *Bs, StageFrags<C> &f, int wm,
+                                           int wn)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+        const int chunk = kk * 2 + half;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+            f.a[kk][i] =
+                *reinterpret_cast<const bf16x8_t *>(As + lds_swz(wm * C::TM + i * 32 + r, chunk));
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            f.b[kk][j] =
+                *reinterpret_cast<const bf16x8_t *>(Bs + lds_swz(wn * C::TN + j * 32 + r, chunk));
+    }
+}
+
+// One LDS stage, 16-deep step by step: each step's fragment reads are
+// followed by its MFMAs, so the compiler can overlap reads and MFMAs.
 template <class C>
 __device__ __forceinline__ void mma_stage(const char *As, const char *Bs,
                                           f32x16_t (&acc)[C::FM][C::FN], int wm, int wn)
@@ -209,6 +290,19 @@ __device__ __forceinline__ void mma_stage(const char *As, const char *Bs,
 }
 
 template <class C>
+__device__ __forceinline__ void mma_frags(const StageFrags<C> &f, f32x16_t (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j],
+                                                                    acc[i][j], 0, 0, 0);
+}
+
+template <class C>
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
 {
 #pragma unroll
@@ -220,28 +314,55 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
                 acc[i][j][r] = 0.0f;
 }
 
-// load(s) issues the global loads of stage s into registers; store(As, Bs)
-// writes them to an LDS stage.  Ends with a barrier (LDS free for reuse).
+// Direct operands are copied HBM -> LDS by DmaLoader (MOEGG_DMA=1) or
+// staged through registers by DirectLoader (MOEGG_DMA=0).
+#ifndef MOEGG_DMA
+#define MOEGG_DMA 0
+#endif
+template <int ROWS, int NT>
+using RowLoader = typename std::conditional<MOEGG_DMA != 0, DmaLoader<ROWS, NT>,
+                                            DirectLoader<ROWS, NT>>::type;
+
+// load(s, As, Bs) starts the HBM reads of stage s (into registers, or
+// straight into the LDS stage As/Bs); store(As, Bs) writes register-staged
+// data to that LDS stage.  Ends with a barrier (LDS free for reuse).
+//
+// With register staging, the reads of stage s+1 are issued first and the
+// MFMAs of each 16-deep step follow their own LDS reads, so LDS reads and
+// MFMAs interleave.  With HBM -> LDS copies, every LDS read of the current
+// stage is issued before the next stage's copies: a read that followed an
+// outstanding copy in program order would have to wait for it, serialising
+// the prefetch with the MFMAs.
 template <class C, class Load, class Store>
-__device__ __forceinline__ void mainloop(char *smem, int nsteps, f32x16_t (&acc)[C::FM][C::FN],
-                                         Load load, Store store)
+__device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
+                                         f32x16_t (&acc)[C::FM][C::FN], Load load, Store store)
 {
     const int wave = threadIdx.x / kWave;
     const int wm = wave / C::WN, wn = wave % C::WN;
     if (nsteps <= 0)
         return;
-    load(0);
-    store(smem, smem + C::A_BYTES);
+    load(0, st0, st0 + C::A_BYTES);
+    store(st0, st0 + C::A_BYTES);
+    wait_vmem();
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
-        char *cur = smem + (s & 1) * C::STAGE;
-        char *nxt = smem + ((s + 1) & 1) * C::STAGE;
+        char *cur = (s & 1) ? st1 : st0;
+        char *nxt = (s & 1) ? st0 : st1;
         const bool more = s + 1 < nsteps;
-        if (more)
-            load(s + 1);
-        mma_stage<C>(cur, cur + C::A_BYTES, acc, wm, wn);
+        if (MOEGG_DMA) {
+            StageFrags<C> f;
+            read_frags<C>(cur, cur + C::A_BYTES, f, wm, wn);
+            if (more)
+                load(s + 1, nxt, nxt + C::A_BYTES);
+            mma_frags<C>(f, acc);
+        } else {
+            if (more)
+                load(s + 1, nxt, nxt + C::A_BYTES);
+            mma_stage<C>(cur, cur + C::A_BYTES, acc, wm, wn);
+        }
         if (more)
             store(nxt, nxt + C::A_BYTES);
+        wait_vmem();
         __syncthreads();
     }
 }
@@ -259,39 +380,68 @@ __device__ __forceinline__ int acc_col(int wn, int j)
     return wn * C::TN + j * 32 + (threadIdx.x & 31);
 }
 
-// bf16 epilogue through LDS.  s_dst[i]: destination row of tile row i (-1:
-// skip), s_scale: optional per-row factor.  Y is bf16 with leading dimension
-// ldy; tile column c maps to output column n0 + c (valid below ncols).
+// bf16 epilogue through LDS.  The tile is staged as bf16 in st0 (or, when
+// it does not fit in one stage, rows [0, BM/2) in st0 and [BM/2, BM) in
+// st1), then copied out as 16-byte row segments.  Each lane addresses its
+// accumulators from one base pointer plus compile-time offsets.
+// s_dst[i]: destination row of tile row i (-1: skip); s_scale: per-row factor
+// applied when `scale` is set.  Y is bf16 with leading dimension ldy; tile
+// column c maps to output column n0 + c (valid below ncols).
 template <class C>
-__device__ __forceinline__ void epilogue_bf16(char *smem, const f32x16_t (&acc)[C::FM][C::FN],
-                                              const int *s_dst, const float *s_scale, char *Y,
-                                              int64_t ldy, int n0, int ncols)
+struct EpiLayout {
+    static constexpr bool SPLIT = C::BM * C::BN * 2 > C::STAGE;
+    static constexpr int ROWS_PER_BUF = SPLIT ? C::BM / 2 : C::BM;
+    static_assert(ROWS_PER_BUF * C::BN * 2 <= C::STAGE, "staged rows must fit in one stage");
+    static_assert(ROWS_PER_BUF % C::TM == 0, "a wave's rows must stay in one staging buffer");
+};
+
+template <class C, bool SCALE>
+__device__ __forceinline__ void stage_bf16(char *st0, char *st1,
+                                           const f32x16_t (&acc)[C::FM][C::FN],
+                                           const float *s_scale)
 {
+    using L = EpiLayout<C>;
     const int wave = threadIdx.x / kWave;
     const int wm = wave / C::WN, wn = wave % C::WN;
-    uint16_t *tile = reinterpret_cast<uint16_t *>(smem);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row0 = wm * C::TM + 4 * (lane >> 5);
+    char *buf = (wm * C::TM) / L::ROWS_PER_BUF ? st1 : st0;
+    uint16_t *base = reinterpret_cast<uint16_t *>(buf) +
+                     (row0 % L::ROWS_PER_BUF) * C::BN + wn * C::TN + (lane & 31);
+    const float *sc = s_scale + row0;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+        for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + 8 * (r >> 2) + (r & 3);  // row offset from row0
+            const float f = SCALE ? sc[rr] : 1.0f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = acc_row<C>(wm, i, r);
-                const int col = acc_col<C>(wn, j);
-                float v = acc[i][j][r];
-                if (s_scale)
-                    v *= s_scale[row];
-                tile[row * C::BN + col] = to_bf16(v);
-            }
+            for (int j = 0; j < C::FN; ++j)
+                base[rr * C::BN + j * 32] = to_bf16(SCALE ? acc[i][j][r] * f : acc[i][j][r]);
+        }
+}
+
+template <class C>
+__device__ __forceinline__ void epilogue_bf16(char *st0, char *st1,
+                                              const f32x16_t (&acc)[C::FM][C::FN],
+                                              const int *s_dst, const float *s_scale, bool scale,
+                                              char *Y, int64_t ldy, int n0, int ncols)
+{
+    using L = EpiLayout<C>;
+    if (scale)
+        stage_bf16<C, true>(st0, st1, acc, s_scale);
+    else
+        stage_bf16<C, false>(st0, st1, acc, s_scale);
     __syncthreads();
     constexpr int CPR = C::BN / 8;  // 16-byte chunks per tile row
     for (int idx = threadIdx.x; idx < C::BM * CPR; idx += C::NT) {
         const int row = idx / CPR, ch = idx % CPR;
         const int dst = s_dst[row];
         const int col = n0 + ch * 8;
+        const char *buf = row / L::ROWS_PER_BUF ? st1 : st0;
         if (dst >= 0 && col < ncols)
             *reinterpret_cast<uint4 *>(Y + ((int64_t)dst * ldy + col) * 2) =
-                *reinterpret_cast<const uint4 *>(smem + (row * C::BN + ch * 8) * 2);
+                *reinterpret_cast<const uint4 *>(buf + ((row % L::ROWS_PER_BUF) * C::BN + ch * 8) * 2);
     }
     __syncthreads();
 }
@@ -373,7 +523,8 @@ __device__ __forceinline__ int checked_gather(const int32_t *gather, int64_t p, 
 template <class C>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 {
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_src[C::BM];
@@ -421,17 +572,15 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
         }
         __syncthreads();
 
-        DirectLoader<C::BM, C::NT> la;
-        DirectLoader<C::BN, C::NT> lb;
+        RowLoader<C::BM, C::NT> la;
+        RowLoader<C::BN, C::NT> lb;
 #pragma unroll
-        for (int i = 0; i < la.RPT; ++i) {
-            const int r = la.tile_row(i);
-            la.set_row(i, r < C::BM ? s_src[r] : -1, row_bytes);
-        }
+        for (int i = 0; i < la.RPT; ++i)
+            la.set_row(i, s_src[la.tile_row(i)], row_bytes);
 #pragma unroll
         for (int i = 0; i < lb.RPT; ++i) {
             const int r = lb.tile_row(i);
-            lb.set_row(i, (r < C::BN && n0 + r < a.N) ? n0 + r : -1, row_bytes);
+            lb.set_row(i, n0 + r < a.N ? n0 + r : -1, row_bytes);
         }
         const __amdgpu_buffer_rsrc_t wr =
             make_rsrc(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
@@ -439,16 +588,16 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         mainloop<C>(
-            smem, nsteps, acc,
-            [&](int s) {
-                la.load(xr, s * BK, a.K);
-                lb.load(wr, s * BK, a.K);
+            st0, st1, nsteps, acc,
+            [&](int s, char *As, char *Bs) {
+                la.load(xr, As, s * BK, a.K);
+                lb.load(wr, Bs, s * BK, a.K);
             },
             [&](char *As, char *Bs) {
                 la.store(As);
                 lb.store(Bs);
             });
-        epilogue_bf16<C>(smem, acc, s_dst, fm ? s_scale : nullptr, a.Y, a.N, n0, a.N);
+        epilogue_bf16<C>(st0, st1, acc, s_dst, s_scale, fm, a.Y, a.N, n0, a.N);
     }
 }
 
@@ -459,7 +608,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 template <class C>
 __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 {
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_src[C::BM];
@@ -500,12 +650,10 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         }
         __syncthreads();
 
-        DirectLoader<C::BM, C::NT> la;
+        RowLoader<C::BM, C::NT> la;
 #pragma unroll
-        for (int i = 0; i < la.RPT; ++i) {
-            const int r = la.tile_row(i);
-            la.set_row(i, r < C::BM ? s_src[r] : -1, dy_row);
-        }
+        for (int i = 0; i < la.RPT; ++i)
+            la.set_row(i, s_src[la.tile_row(i)], dy_row);
         TransLoader<C::BN, C::NT> lb;
         const __amdgpu_buffer_rsrc_t wr =
             make_rsrc(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
@@ -515,16 +663,16 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         mainloop<C>(
-            smem, nsteps, acc,
-            [&](int s) {
-                la.load(dyr, s * BK, a.N);
+            st0, st1, nsteps, acc,
+            [&](int s, char *As, char *) {
+                la.load(dyr, As, s * BK, a.N);
                 lb.load(wr, s * BK, k0, a.K, wrowfn);
             },
             [&](char *As, char *Bs) {
                 la.store(As);
                 lb.store(Bs);
             });
-        epilogue_bf16<C>(smem, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, a.dX, a.K, k0, a.K);
     }
 }
 
@@ -535,7 +683,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 template <class C>
 __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
 {
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_order[kMaxExperts];
@@ -601,8 +750,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         mainloop<C>(
-            smem, (mc + BK - 1) / BK, acc,
-            [&](int s) {
+            st0, st1, (mc + BK - 1) / BK, acc,
+            [&](int s, char *, char *) {
                 la.load(dyr, s * BK, n0, a.N, dyrowfn);
                 lb.load(xr, s * BK, k0, a.K, xrowfn);
             },
@@ -613,7 +762,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         if (f32out)
             epilogue_f32<C>(acc, s_dst, reinterpret_cast<float *>(a.dW), a.K, k0, a.K);
         else
-            epilogue_bf16<C>(smem, acc, s_dst, nullptr, a.dW, a.K, k0, a.K);
+            epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, a.dW, a.K, k0, a.K);
     }
 }
 
@@ -624,7 +773,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
 template <class C, bool TRANS_B>
 __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
 {
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
     __shared__ int s_tstart[MOEGG_MAX_GROUPS + 1];
     __shared__ int s_dst[C::BM];
 
@@ -655,28 +805,28 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
         const int64_t x_row = (int64_t)g.ldx * 2, w_row = (int64_t)g.ldw * 2;
         const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)g.m * x_row);
         const __amdgpu_buffer_rsrc_t wr = make_rsrc(g.w, (int64_t)(TRANS_B ? g.n : g.k) * w_row);
-        DirectLoader<C::BM, C::NT> la;
+        RowLoader<C::BM, C::NT> la;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i) {
             const int r = la.tile_row(i);
-            la.set_row(i, (r < C::BM && m0 + r < g.m) ? m0 + r : -1, x_row);
+            la.set_row(i, m0 + r < g.m ? m0 + r : -1, x_row);
         }
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         const int nsteps = (g.k + BK - 1) / BK;
         const int kk = g.k;
         if constexpr (TRANS_B) {
-            DirectLoader<C::BN, C::NT> lb;
+            RowLoader<C::BN, C::NT> lb;
 #pragma unroll
             for (int i = 0; i < lb.RPT; ++i) {
                 const int r = lb.tile_row(i);
-                lb.set_row(i, (r < C::BN && n0 + r < g.n) ? n0 + r : -1, w_row);
+                lb.set_row(i, n0 + r < g.n ? n0 + r : -1, w_row);
             }
             mainloop<C>(
-                smem, nsteps, acc,
-                [&](int s) {
-                    la.load(xr, s * BK, kk);
-                    lb.load(wr, s * BK, kk);
+                st0, st1, nsteps, acc,
+                [&](int s, char *As, char *Bs) {
+                    la.load(xr, As, s * BK, kk);
+                    lb.load(wr, Bs, s * BK, kk);
                 },
                 [&](char *As, char *Bs) {
                     la.store(As);
@@ -689,17 +839,18 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
             };
             const int n = g.n;
             mainloop<C>(
-                smem, nsteps, acc,
-                [&](int s) {
-                    la.load(xr, s * BK, kk);
+                st0, st1, nsteps, acc,
+                [&](int s, char *As, char *) {
+                    la.load(xr, As, s * BK, kk);
                     lb.load(wr, s * BK, n0, n, wrowfn);
                 },
                 [&](char *As, char *Bs) {
-                    la.store(As);
-                    lb.store(Bs);
-                });
+                la.store(As);
+                lb.store(Bs);
+            });
         }
-        epilogue_bf16<C>(smem, acc, s_dst, nullptr, static_cast<char *>(g.y), g.ldy, n0, g.n);
+        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, static_cast<char *>(g.y), g.ldy, n0,
+                         g.n);
     }
 }
 
@@ -707,9 +858,32 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
 // Host launchers
 // ---------------------------------------------------------------------------
 
-using BigCfg = Cfg<256, 256, 2, 4>;    // 512 threads, 128 KiB of operand LDS
-using SmallCfg = Cfg<32, 128, 1, 4>;   // few rows per expert: stream the weights
-using GroupCfg = Cfg<128, 128, 2, 2>;  // small explicit groups: more tiles
+// Tile shapes: <BM, BN, waves along M, waves along N>.
+#ifndef MOEGG_FWD_CFG
+#define MOEGG_FWD_CFG 256, 256, 2, 4
+#endif
+#ifndef MOEGG_DX_CFG
+#define MOEGG_DX_CFG 256, 256, 2, 4
+#endif
+#ifndef MOEGG_DW_CFG
+#define MOEGG_DW_CFG 256, 256, 2, 4
+#endif
+#ifndef MOEGG_SMALL_CFG
+#define MOEGG_SMALL_CFG 32, 128, 1, 4
+#endif
+using BigCfg = Cfg<MOEGG_FWD_CFG>;       // many rows per expert
+using DxCfg = Cfg<MOEGG_DX_CFG>;
+using DwCfg = Cfg<MOEGG_DW_CFG>;
+using SmallCfg = Cfg<MOEGG_SMALL_CFG>;   // few rows per expert: stream the weights
+using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
+
+// Explicit instantiations: every kernel the launchers use is emitted here.
+template __global__ void fwd_kernel<BigCfg>(FwdParams);
+template __global__ void fwd_kernel<SmallCfg>(FwdParams);
+template __global__ void dx_kernel<DxCfg>(DxParams);
+template __global__ void dw_kernel<DwCfg>(DwParams);
+template __global__ void groups_kernel<GroupCfg, true>(GroupsParams);
+template __global__ void groups_kernel<GroupCfg, false>(GroupsParams);
 
 static int64_t n_blocks_bound(int64_t rows, int E, int block)
 {
@@ -754,7 +928,7 @@ hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream)
 
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 {
-    using C = BigCfg;
+    using C = DxCfg;
     const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.K + C::BN - 1) / C::BN);
     static int res = resident_blocks(dx_kernel<C>, C::NT);
     hipLaunchKernelGGL(dx_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
@@ -763,7 +937,7 @@ hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 
 hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
 {
-    using C = BigCfg;
+    using C = DwCfg;
     const int64_t tiles =
         (int64_t)p.E * ((p.N + C::BM - 1) / C::BM) * ((p.K + C::BN - 1) / C::BN);
     static int res = resident_blocks(dw_kernel<C>, C::NT);

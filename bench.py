@@ -235,6 +235,19 @@ def cpu_baseline(st, budget_s):
             "sample": sample, "seconds": round(dt, 3)}
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: each launch reads and writes nbytes."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +256,8 @@ def main():
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for the baseline (0 disables)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
@@ -252,6 +267,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        return copy_calibration()
     mg.load_library()
 
     st = make_step(args.workload)

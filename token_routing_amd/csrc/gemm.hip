@@ -46,9 +46,19 @@ namespace moegg {
 constexpr int BK = 64;
 constexpr int kChunks = BK / 8;  // 16-byte chunks per LDS row
 
+// LDS tile rows are 128 bytes (64 bf16).  gfx950 serves a 16-byte-per-lane
+// LDS access 16 lanes (256 bytes, 64 banks) at a time, so 16 consecutive rows
+// read at one logical chunk must fall in 16 distinct 16-byte bank groups:
+// even and odd rows occupy the two 128-byte halves, and XOR-ing the chunk
+// with (row / 2) % 8 spreads each parity class over all 8 groups of its half.
+__device__ __forceinline__ int swz_chunk(int row, int chunk)
+{
+    return chunk ^ ((row >> 1) & 7);
+}
+
 __device__ __forceinline__ int lds_swz(int row, int chunk)
 {
-    return row * (BK * 2) + ((chunk ^ (row & 7)) << 4);
+    return row * (BK * 2) + (swz_chunk(row, chunk) << 4);
 }
 
 template <int BM_, int BN_, int WM_, int WN_>
@@ -129,9 +139,10 @@ struct DirectLoader {
 // passing through registers (buffer_load_dwordx4 ... lds).  Lane l of a wave
 // writes LDS bytes [16 l, 16 l + 16) of the wave's 1 KiB window, i.e. physical
 // chunk l % 8 of window row l / 8; to land in the swizzled layout it fetches
-// logical chunk (l % 8) ^ (row % 8) = (l % 8) ^ (l / 8).  Wave w, pass i
-// fills rows 8 w + i * (NT / 8) .. + 7, so the eight lanes of a row still read
-// one whole 128-byte row segment.
+// the logical chunk that swizzles to it (the swizzle is an involution).  Wave
+// w, pass i fills rows 8 w + i * (NT / 8) .. + 7 (a window starting at a
+// multiple of 16 rows for even w), so the eight lanes of a row still read one
+// whole 128-byte row segment.
 template <int ROWS, int NT>
 struct DmaLoader {
     static constexpr int PASS = NT / kChunks;
@@ -140,10 +151,12 @@ struct DmaLoader {
     uint32_t off[RPT];
 
     __device__ __forceinline__ static int tile_row(int i) { return (threadIdx.x >> 3) + i * PASS; }
+    // Lane l of wave w fills row 8 w + l / 8 + i * PASS (PASS is a multiple of
+    // 16, so the swizzle depends only on threadIdx.x / 8) at physical chunk l % 8.
+    static_assert(PASS % 16 == 0, "swizzle period");
     __device__ __forceinline__ static int chunk()
     {
-        const int l = threadIdx.x & (kWave - 1);
-        return (l & 7) ^ (l >> 3);
+        return swz_chunk(threadIdx.x >> 3, threadIdx.x & 7);
     }
 
     __device__ __forceinline__ void set_row(int i, int64_t row, int64_t row_bytes)
@@ -175,60 +188,78 @@ __device__ __forceinline__ void wait_vmem()
     __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// COLS tile rows whose reduction index runs across HBM rows.  The stage is
-// (BK / 8) x (COLS / 8) blocks of 8 x 8 elements; block b of thread t is
-// blk = t + b * NT with reduction block blk % 8 and column block blk / 8.
-// rowfn(red) gives the byte offset of the HBM row holding reduction index
-// red (kOOB: zeros).
+// Operands whose reduction index runs across HBM rows (W in dX, dY and X in
+// dW, a [K, N] weight in the groups) are kept in LDS as they are in HBM: BK
+// reduction rows of COLS bf16 (row pitch 2 COLS bytes).  The MFMA fragments
+// are then read with the gfx950 LDS transpose read (tr_frag below).  16-byte
+// chunk c of row r is stored at chunk c ^ ((r % 4) * 4), so the four rows one
+// transpose read touches fall in four different 64-byte bank groups.
+template <int COLS>
+__device__ __forceinline__ int tr_off(int row, int chunk)
+{
+    static_assert(COLS >= 128, "the row swizzle needs 16 chunks per row");
+    return row * (COLS * 2) + ((chunk ^ ((row & 3) << 2)) << 4);
+}
+
+// Copies BK reduction rows x COLS columns, 16 bytes per lane, consecutive
+// lanes along a row (whole 128-byte row segments).  rowfn(red) gives the
+// byte offset of the HBM row holding reduction index red (kOOB: zeros).
 template <int COLS, int NT>
-struct TransLoader {
-    static constexpr int NBLK = (BK / 8) * (COLS / 8);
-    static constexpr int BPT = (NBLK + NT - 1) / NT;
-    uint4 v[BPT][8];
+struct RowTileLoader {
+    static constexpr int CPR = COLS / 8;
+    static constexpr int ROWS_PER_PASS = NT / CPR;
+    static constexpr int RPT = BK / ROWS_PER_PASS;
+    static_assert(NT % CPR == 0 && BK % ROWS_PER_PASS == 0, "whole rows per pass");
+    uint4 v[RPT];
 
     template <class RowFn>
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int red0, int col0, int ncols,
                                          RowFn rowfn)
     {
+        const int col = col0 + (threadIdx.x % CPR) * 8;
+        const bool cin = col < ncols;
 #pragma unroll
-        for (int b = 0; b < BPT; ++b) {
-            const int blk = threadIdx.x + b * NT;
-            const int rb = blk & 7, cb = blk >> 3;
-            const int col = col0 + cb * 8;
-            const bool cin = (NBLK % NT == 0 || blk < NBLK) && col < ncols;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t ro = rowfn(red0 + rb * 8 + j);
-                v[b][j] = buf_load16(r, cin ? ro + (uint32_t)col * 2 : kOOB, 0);
-            }
+        for (int i = 0; i < RPT; ++i) {
+            const uint32_t ro = rowfn(red0 + (int)threadIdx.x / CPR + i * ROWS_PER_PASS);
+            v[i] = buf_load16(r, cin ? ro + (uint32_t)col * 2 : kOOB, 0);
         }
     }
 
     __device__ __forceinline__ void store(char *lds) const
     {
+        const int c = threadIdx.x % CPR;
 #pragma unroll
-        for (int b = 0; b < BPT; ++b) {
-            const int blk = threadIdx.x + b * NT;
-            if (NBLK % NT != 0 && blk >= NBLK)
-                continue;
-            const int rb = blk & 7, cb = blk >> 3;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // column i of the 8 x 8 block: element i of rows 0..7
-                const int d = i >> 1;
-                uint32_t o[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t lo = dw(v[b][2 * q], d), hi = dw(v[b][2 * q + 1], d);
-                    o[q] = (i & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                   : ((lo & 0xffffu) | (hi << 16));
-                }
-                *reinterpret_cast<uint4 *>(lds + lds_swz(cb * 8 + i, rb)) =
-                    make_uint4(o[0], o[1], o[2], o[3]);
-            }
-        }
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<uint4 *>(lds + tr_off<COLS>((int)threadIdx.x / CPR + i * ROWS_PER_PASS,
+                                                           c)) = v[i];
     }
 };
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+// MFMA fragment (8 reduction elements of one column, lane layout of
+// v_mfma_f32_32x32x16_bf16) of columns [c0, c0 + 32), reduction rows
+// [16 kk, 16 kk + 16), from a row-major LDS tile.  ds_read_b64_tr_b16: in
+// each 16-lane group, lane i receives element i % 4 of the 8 bytes addressed
+// by lanes 4 j + i / 4 (j = 0..3).  Lane q of a group addresses reduction row
+// q / 4 and columns 4 (q % 4) .. + 3 of its 16-column half, so lane i gets
+// column i and four consecutive reduction rows; two reads give eight.
+template <int COLS>
+__device__ __forceinline__ bf16x8_t tr_frag(const char *tile, int kk, int c0)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int q = lane & 15;
+    const int row = kk * 16 + 8 * (lane >> 5) + (q >> 2);
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+    const int within = (col & 7) * 2;
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(tile + tr_off<COLS>(row, col >> 3) + within));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16 *)(tile + tr_off<COLS>(row + 4, col >> 3) + within));
+    const v4i16_t both[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8_t, both);
+}
 
 // ---------------------------------------------------------------------------
 // MFMA stage and mainloop
@@ -263,30 +294,77 @@ __device__ __forceinline__ void read_frags(const char *As, const char *Bs, Stage
     }
 }
 
-// One LDS stage, 16-deep step by step: each step's fragment reads are
-// followed by its MFMAs, so the compiler can overlap reads and MFMAs.
+// One LDS stage, software-pipelined over its four 16-deep steps: the
+// fragment reads of step kk+1 are issued before the MFMAs of step kk, so each
+// wave's LDS latency overlaps its own MFMAs (two fragment register sets).
+// Fragments of one 16-deep step.  A_TR / B_TR: the operand's LDS tile is
+// row-major (reduction rows) and is read with transpose reads; otherwise it
+// is reduction-contiguous (lds_swz layout).
+template <class C, bool A_TR, bool B_TR>
+__device__ __forceinline__ void read_step(const char *As, const char *Bs, int kk, int wm, int wn,
+                                          bf16x8_t (&a)[C::FM], bf16x8_t (&b)[C::FN])
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 31, chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        if constexpr (A_TR)
+            a[i] = tr_frag<C::BM>(As, kk, wm * C::TM + i * 32);
+        else
+            a[i] = *reinterpret_cast<const bf16x8_t *>(As + lds_swz(wm * C::TM + i * 32 + r, chunk));
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        if constexpr (B_TR)
+            b[j] = tr_frag<C::BN>(Bs, kk, wn * C::TN + j * 32);
+        else
+            b[j] = *reinterpret_cast<const bf16x8_t *>(Bs + lds_swz(wn * C::TN + j * 32 + r, chunk));
+    }
+}
+
 template <class C>
+__device__ __forceinline__ void mma_step(const bf16x8_t (&a)[C::FM], const bf16x8_t (&b)[C::FN],
+                                         f32x16_t (&acc)[C::FM][C::FN])
+{
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// PIPE = false: each step's reads directly precede its MFMAs (fewer live
+// registers, for kernels that also hold register-staged operands).
+template <class C, bool PIPE, bool A_TR, bool B_TR>
 __device__ __forceinline__ void mma_stage(const char *As, const char *Bs,
                                           f32x16_t (&acc)[C::FM][C::FN], int wm, int wn)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = lane & 31, half = lane >> 5;
+    if (!PIPE) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        const int chunk = kk * 2 + half;
-        bf16x8_t a[C::FM], b[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            a[i] = *reinterpret_cast<const bf16x8_t *>(As + lds_swz(wm * C::TM + i * 32 + r, chunk));
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            b[j] = *reinterpret_cast<const bf16x8_t *>(Bs + lds_swz(wn * C::TN + j * 32 + r, chunk));
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            bf16x8_t a[C::FM], b[C::FN];
+            read_step<C, A_TR, B_TR>(As, Bs, kk, wm, wn, a, b);
+            mma_step<C>(a, b, acc);
+        }
+        return;
     }
+    // sched_barrier(0) keeps the compiler from moving the reads back next to
+    // their consumers.
+    bf16x8_t a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+    read_step<C, A_TR, B_TR>(As, Bs, 0, wm, wn, a0, b0);
+    read_step<C, A_TR, B_TR>(As, Bs, 1, wm, wn, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<C>(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step<C, A_TR, B_TR>(As, Bs, 2, wm, wn, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<C>(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step<C, A_TR, B_TR>(As, Bs, 3, wm, wn, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<C>(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step<C>(a1, b1, acc);
 }
 
 template <class C>
@@ -333,7 +411,7 @@ using RowLoader = typename std::conditional<MOEGG_DMA != 0, DmaLoader<ROWS, NT>,
 // stage is issued before the next stage's copies: a read that followed an
 // outstanding copy in program order would have to wait for it, serialising
 // the prefetch with the MFMAs.
-template <class C, class Load, class Store>
+template <class C, bool PIPE, bool A_TR, bool B_TR, class Load, class Store>
 __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
                                          f32x16_t (&acc)[C::FM][C::FN], Load load, Store store)
 {
@@ -358,7 +436,7 @@ __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
         } else {
             if (more)
                 load(s + 1, nxt, nxt + C::A_BYTES);
-            mma_stage<C>(cur, cur + C::A_BYTES, acc, wm, wn);
+            mma_stage<C, PIPE, A_TR, B_TR>(cur, cur + C::A_BYTES, acc, wm, wn);
         }
         if (more)
             store(nxt, nxt + C::A_BYTES);
@@ -587,7 +665,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        mainloop<C>(
+        mainloop<C, true, false, false>(
             st0, st1, nsteps, acc,
             [&](int s, char *As, char *Bs) {
                 la.load(xr, As, s * BK, a.K);
@@ -654,7 +732,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], dy_row);
-        TransLoader<C::BN, C::NT> lb;
+        RowTileLoader<C::BN, C::NT> lb;
         const __amdgpu_buffer_rsrc_t wr =
             make_rsrc(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
         const int N = a.N;
@@ -662,7 +740,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        mainloop<C>(
+        mainloop<C, true, false, true>(
             st0, st1, nsteps, acc,
             [&](int s, char *As, char *) {
                 la.load(dyr, As, s * BK, a.N);
@@ -679,6 +757,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 // ---------------------------------------------------------------------------
 // dW_e = dY_e^T X_e  (reduction over the expert's own rows)
 // ---------------------------------------------------------------------------
+
+constexpr int kGroupK = 8;
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
@@ -716,8 +796,14 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
 
     for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
         const int e = __builtin_amdgcn_readfirstlane(s_order[t / per_expert]);
+        // Grouped raster inside the expert: runs of up to kGroupK K-panels per
+        // N column, so consecutive tiles (one XCD's concurrent set) share
+        // few dY (N) and X (K) panels in that XCD's L2.
         const int u = t % per_expert;
-        const int nt = u % ntn, kt = u / ntn;
+        const int span = kGroupK * ntn;
+        const int first_kt = (u / span) * kGroupK;
+        const int gk = min(ntk - first_kt, kGroupK);
+        const int kt = first_kt + (u % span) % gk, nt = (u % span) / gk;
         const int n0 = nt * C::BM, k0 = kt * C::BN;
         const int start = __builtin_amdgcn_readfirstlane(s_roff[e]);
         const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1]) - start;
@@ -745,11 +831,11 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
             const int g = px ? checked_gather(gather, p, S, err) : (int)p;
             return g >= 0 ? (uint32_t)((px ? g / topk : g) * x_row) : kOOB;
         };
-        TransLoader<C::BM, C::NT> la;
-        TransLoader<C::BN, C::NT> lb;
+        RowTileLoader<C::BM, C::NT> la;
+        RowTileLoader<C::BN, C::NT> lb;
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        mainloop<C>(
+        mainloop<C, true, true, true>(
             st0, st1, (mc + BK - 1) / BK, acc,
             [&](int s, char *, char *) {
                 la.load(dyr, s * BK, n0, a.N, dyrowfn);
@@ -822,7 +908,7 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
                 const int r = lb.tile_row(i);
                 lb.set_row(i, n0 + r < g.n ? n0 + r : -1, w_row);
             }
-            mainloop<C>(
+            mainloop<C, true, false, false>(
                 st0, st1, nsteps, acc,
                 [&](int s, char *As, char *Bs) {
                     la.load(xr, As, s * BK, kk);
@@ -833,12 +919,12 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
                     lb.store(Bs);
                 });
         } else {
-            TransLoader<C::BN, C::NT> lb;
+            RowTileLoader<C::BN, C::NT> lb;
             auto wrowfn = [=](int red) -> uint32_t {
                 return red < kk ? (uint32_t)(red * w_row) : kOOB;
             };
             const int n = g.n;
-            mainloop<C>(
+            mainloop<C, true, false, true>(
                 st0, st1, nsteps, acc,
                 [&](int s, char *As, char *) {
                     la.load(xr, As, s * BK, kk);

@@ -93,6 +93,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(const u32x4_t &w)
+{
+    const uint64_t base = (uint64_t)w.x | ((uint64_t)w.y << 32);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), (short)0, (int)w.z,
+                                             (int)w.w);
+}
+
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -117,8 +126,11 @@ struct DirectLoader {
         off[i] = row < 0 ? kOOB : (uint32_t)(row * row_bytes) + (threadIdx.x & 7) * 16;
     }
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char *, int k0, int klen)
+    static constexpr bool kAsync = false;
+
+    __device__ __forceinline__ void load(const u32x4_t &w, char *, int k0, int klen)
     {
+        const __amdgpu_buffer_rsrc_t r = as_rsrc(w);
         const bool kin = k0 + (int)(threadIdx.x & 7) * 8 < klen;
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
@@ -140,17 +152,48 @@ struct DirectLoader {
 // writes LDS bytes [16 l, 16 l + 16) of the wave's 1 KiB window, i.e. physical
 // chunk l % 8 of window row l / 8; to land in the swizzled layout it fetches
 // the logical chunk that swizzles to it (the swizzle is an involution).  Wave
-// w, pass i fills rows 8 w + i * (NT / 8) .. + 7 (a window starting at a
-// multiple of 16 rows for even w), so the eight lanes of a row still read one
-// whole 128-byte row segment.
+// w, pass i fills rows 8 w + i * (NT / 8) .. + 7, so the eight lanes of a row
+// still read one whole 128-byte row segment.
+//
+// The copy is issued from inline assembly, so the compiler does not know it
+// writes LDS and does not hold back LDS reads of the other stage until it
+// lands; the mainloop waits for it explicitly (wait_vmem) before the barrier
+// that publishes the stage.  Vector-memory loads complete in issue order, so
+// any wait the compiler inserts for its own loads can only wait longer.
+// Raw buffer descriptor words (uniform): base, stride 0, num_records, format.
+__device__ __forceinline__ u32x4_t rsrc_words(const void *base, int64_t bytes)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    u32x4_t w;
+    w.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    w.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+    w.z = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+    w.w = 0x00020000u;
+    return w;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const u32x4_t &r, uint32_t voff, uint32_t soff,
+                                              uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int ROWS, int NT>
 struct DmaLoader {
     static constexpr int PASS = NT / kChunks;
     static constexpr int RPT = ROWS / PASS;
     static_assert(ROWS % PASS == 0, "DMA loader covers whole passes");
+    static constexpr bool kAsync = true;
     uint32_t off[RPT];
 
     __device__ __forceinline__ static int tile_row(int i) { return (threadIdx.x >> 3) + i * PASS; }
+
     // Lane l of wave w fills row 8 w + l / 8 + i * PASS (PASS is a multiple of
     // 16, so the swizzle depends only on threadIdx.x / 8) at physical chunk l % 8.
     static_assert(PASS % 16 == 0, "swizzle period");
@@ -167,17 +210,16 @@ struct DmaLoader {
     __device__ __forceinline__ void store(char *) const {}
 
     // Enqueue the copies of reduction stage k0 into the LDS stage `lds`.
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char *lds, int k0, int klen) const
+    __device__ __forceinline__ void load(const u32x4_t &r, char *lds, int k0, int klen) const
     {
         const bool kin = k0 + chunk() * 8 < klen;
-        const int wave_row = (threadIdx.x / kWave) * 8;
+        const uint32_t wave_row = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * 8;
+        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char *)lds);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            char *dst = lds + (i * PASS + wave_row) * (BK * 2);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void *)dst, 16, kin ? off[i] : kOOB,
-                (uint32_t)k0 * 2, 0, 0);
-        }
+        for (int i = 0; i < RPT; ++i)
+            copy16_to_lds(r, kin ? off[i] : kOOB, (uint32_t)k0 * 2,
+                          __builtin_amdgcn_readfirstlane(base + (i * PASS + wave_row) * (BK * 2)));
     }
 };
 
@@ -185,7 +227,7 @@ struct DmaLoader {
 // HBM -> LDS copies) have completed: s_waitcnt vmcnt(0), other counters free.
 __device__ __forceinline__ void wait_vmem()
 {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // Operands whose reduction index runs across HBM rows (W in dX, dY and X in
@@ -213,9 +255,10 @@ struct RowTileLoader {
     uint4 v[RPT];
 
     template <class RowFn>
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int red0, int col0, int ncols,
+    __device__ __forceinline__ void load(const u32x4_t &w, int red0, int col0, int ncols,
                                          RowFn rowfn)
     {
+        const __amdgpu_buffer_rsrc_t r = as_rsrc(w);
         const int col = col0 + (threadIdx.x % CPR) * 8;
         const bool cin = col < ncols;
 #pragma unroll
@@ -265,38 +308,6 @@ __device__ __forceinline__ bf16x8_t tr_frag(const char *tile, int kk, int c0)
 // MFMA stage and mainloop
 // ---------------------------------------------------------------------------
 
-// All MFMA operands of one LDS stage, read into registers: lane l holds 8
-// reduction elements of tile row (l % 32) of each 32-row block, for the four
-// 16-deep MFMA steps of the stage.
-template <class C>
-struct StageFrags {
-    bf16x8_t a[BK / 16][C::FM];
-    bf16x8_t b[BK / 16][C::FN];
-};
-
-template <class C>
-__device__ __forceinline__ void read_frags(const char *As, const char *Bs, StageFrags<C> &f, int wm,
-                                           int wn)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        const int chunk = kk * 2 + half;
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-            f.a[kk][i] =
-                *reinterpret_cast<const bf16x8_t *>(As + lds_swz(wm * C::TM + i * 32 + r, chunk));
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-            f.b[kk][j] =
-                *reinterpret_cast<const bf16x8_t *>(Bs + lds_swz(wn * C::TN + j * 32 + r, chunk));
-    }
-}
-
-// One LDS stage, software-pipelined over its four 16-deep steps: the
-// fragment reads of step kk+1 are issued before the MFMAs of step kk, so each
-// wave's LDS latency overlaps its own MFMAs (two fragment register sets).
 // Fragments of one 16-deep step.  A_TR / B_TR: the operand's LDS tile is
 // row-major (reduction rows) and is read with transpose reads; otherwise it
 // is reduction-contiguous (lds_swz layout).
@@ -368,19 +379,6 @@ __device__ __forceinline__ void mma_stage(const char *As, const char *Bs,
 }
 
 template <class C>
-__device__ __forceinline__ void mma_frags(const StageFrags<C> &f, f32x16_t (&acc)[C::FM][C::FN])
-{
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j],
-                                                                    acc[i][j], 0, 0, 0);
-}
-
-template <class C>
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
 {
 #pragma unroll
@@ -392,25 +390,29 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
                 acc[i][j][r] = 0.0f;
 }
 
-// Direct operands are copied HBM -> LDS by DmaLoader (MOEGG_DMA=1) or
-// staged through registers by DirectLoader (MOEGG_DMA=0).
-#ifndef MOEGG_DMA
-#define MOEGG_DMA 0
+// Direct operands are copied HBM -> LDS by DmaLoader (ASYNC) or staged
+// through registers by DirectLoader.  Measured on MI355X: the copies are
+// faster in the forward (both operands direct); in dX, whose other operand is
+// register-staged, register staging of both is faster.
+#ifndef MOEGG_FWD_DMA
+#define MOEGG_FWD_DMA 1
 #endif
-template <int ROWS, int NT>
-using RowLoader = typename std::conditional<MOEGG_DMA != 0, DmaLoader<ROWS, NT>,
-                                            DirectLoader<ROWS, NT>>::type;
+#ifndef MOEGG_DX_DMA
+#define MOEGG_DX_DMA 0
+#endif
+#ifndef MOEGG_GROUPS_DMA
+#define MOEGG_GROUPS_DMA 1
+#endif
+template <int ROWS, int NT, bool ASYNC>
+using RowLoader =
+    typename std::conditional<ASYNC, DmaLoader<ROWS, NT>, DirectLoader<ROWS, NT>>::type;
 
-// load(s, As, Bs) starts the HBM reads of stage s (into registers, or
-// straight into the LDS stage As/Bs); store(As, Bs) writes register-staged
-// data to that LDS stage.  Ends with a barrier (LDS free for reuse).
-//
-// With register staging, the reads of stage s+1 are issued first and the
-// MFMAs of each 16-deep step follow their own LDS reads, so LDS reads and
-// MFMAs interleave.  With HBM -> LDS copies, every LDS read of the current
-// stage is issued before the next stage's copies: a read that followed an
-// outstanding copy in program order would have to wait for it, serialising
-// the prefetch with the MFMAs.
+// Two LDS stages.  Per stage s: start the HBM reads of stage s+1 (copies
+// straight into the other LDS stage, or loads into registers), run the MFMAs
+// of stage s from LDS, write register-staged data of stage s+1 to LDS, wait
+// for this wave's reads and copies, and barrier.  load(s, As, Bs) starts the
+// reads of stage s; store(As, Bs) writes register-staged data.  The other
+// stage was last read before the previous barrier, so it is free to fill.
 template <class C, bool PIPE, bool A_TR, bool B_TR, class Load, class Store>
 __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
                                          f32x16_t (&acc)[C::FM][C::FN], Load load, Store store)
@@ -427,17 +429,9 @@ __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
         char *cur = (s & 1) ? st1 : st0;
         char *nxt = (s & 1) ? st0 : st1;
         const bool more = s + 1 < nsteps;
-        if (MOEGG_DMA) {
-            StageFrags<C> f;
-            read_frags<C>(cur, cur + C::A_BYTES, f, wm, wn);
-            if (more)
-                load(s + 1, nxt, nxt + C::A_BYTES);
-            mma_frags<C>(f, acc);
-        } else {
-            if (more)
-                load(s + 1, nxt, nxt + C::A_BYTES);
-            mma_stage<C, PIPE, A_TR, B_TR>(cur, cur + C::A_BYTES, acc, wm, wn);
-        }
+        if (more)
+            load(s + 1, nxt, nxt + C::A_BYTES);
+        mma_stage<C, PIPE, A_TR, B_TR>(cur, cur + C::A_BYTES, acc, wm, wn);
         if (more)
             store(nxt, nxt + C::A_BYTES);
         wait_vmem();
@@ -618,7 +612,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
     const int nsteps = (a.K + BK - 1) / BK;
     const int64_t row_bytes = (int64_t)a.K * 2;
     const int64_t x_rows = px ? a.S / a.topk : a.S;
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, x_rows * row_bytes);
+    const u32x4_t xr = rsrc_words(a.X, x_rows * row_bytes);
 
     for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
         const int e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
@@ -650,8 +644,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
         }
         __syncthreads();
 
-        RowLoader<C::BM, C::NT> la;
-        RowLoader<C::BN, C::NT> lb;
+        RowLoader<C::BM, C::NT, MOEGG_FWD_DMA != 0> la;
+        RowLoader<C::BN, C::NT, MOEGG_FWD_DMA != 0> lb;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], row_bytes);
@@ -660,8 +654,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             const int r = lb.tile_row(i);
             lb.set_row(i, n0 + r < a.N ? n0 + r : -1, row_bytes);
         }
-        const __amdgpu_buffer_rsrc_t wr =
-            make_rsrc(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
+        const u32x4_t wr =
+            rsrc_words(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
 
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
@@ -700,7 +694,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                                           [&](int m) { return (m + C::BM - 1) / C::BM * ntk; });
     const int nsteps = (a.N + BK - 1) / BK;
     const int64_t dy_row = (int64_t)a.N * 2, w_row = (int64_t)a.K * 2;
-    const __amdgpu_buffer_rsrc_t dyr = make_rsrc(a.dY, a.S * dy_row);
+    const u32x4_t dyr = rsrc_words(a.dY, a.S * dy_row);
 
     for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
         const int e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
@@ -728,13 +722,13 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         }
         __syncthreads();
 
-        RowLoader<C::BM, C::NT> la;
+        RowLoader<C::BM, C::NT, MOEGG_DX_DMA != 0> la;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], dy_row);
         RowTileLoader<C::BN, C::NT> lb;
-        const __amdgpu_buffer_rsrc_t wr =
-            make_rsrc(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
+        const u32x4_t wr =
+            rsrc_words(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
         const int N = a.N;
         auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
 
@@ -791,8 +785,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
     const int total = a.E * per_expert;
     const int64_t dy_row = (int64_t)a.N * 2, x_row = (int64_t)a.K * 2;
     const int64_t x_rows = px ? a.S / a.topk : a.S;
-    const __amdgpu_buffer_rsrc_t dyr = make_rsrc(a.dY, a.S * dy_row);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.X, x_rows * x_row);
+    const u32x4_t dyr = rsrc_words(a.dY, a.S * dy_row);
+    const u32x4_t xr = rsrc_words(a.X, x_rows * x_row);
 
     for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
         const int e = __builtin_amdgcn_readfirstlane(s_order[t / per_expert]);
@@ -889,9 +883,9 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
         __syncthreads();
 
         const int64_t x_row = (int64_t)g.ldx * 2, w_row = (int64_t)g.ldw * 2;
-        const __amdgpu_buffer_rsrc_t xr = make_rsrc(g.x, (int64_t)g.m * x_row);
-        const __amdgpu_buffer_rsrc_t wr = make_rsrc(g.w, (int64_t)(TRANS_B ? g.n : g.k) * w_row);
-        RowLoader<C::BM, C::NT> la;
+        const u32x4_t xr = rsrc_words(g.x, (int64_t)g.m * x_row);
+        const u32x4_t wr = rsrc_words(g.w, (int64_t)(TRANS_B ? g.n : g.k) * w_row);
+        RowLoader<C::BM, C::NT, MOEGG_GROUPS_DMA != 0> la;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i) {
             const int r = la.tile_row(i);
@@ -902,7 +896,7 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
         const int nsteps = (g.k + BK - 1) / BK;
         const int kk = g.k;
         if constexpr (TRANS_B) {
-            RowLoader<C::BN, C::NT> lb;
+            RowLoader<C::BN, C::NT, MOEGG_GROUPS_DMA != 0> lb;
 #pragma unroll
             for (int i = 0; i < lb.RPT; ++i) {
                 const int r = lb.tile_row(i);

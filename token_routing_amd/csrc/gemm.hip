@@ -278,6 +278,59 @@ struct RowTileLoader {
     }
 };
 
+// The same row-major tile, copied HBM -> LDS without registers.  A wave's
+// 1 KiB window is RW = 64 / (COLS / 8) whole rows; lane l writes physical
+// chunk l % (COLS / 8) of window row l / (COLS / 8) and therefore fetches the
+// logical chunk that the row swizzle maps there.  Row indices for the next
+// stage are fetched one stage ahead (fetch), so a gathered row index (one
+// global load) is in registers before its row is copied (load).
+template <int COLS, int NT>
+struct TileDmaLoader {
+    static constexpr int CPR = COLS / 8;
+    static constexpr int RW = kWave / CPR;
+    static constexpr int NWAVE = NT / kWave;
+    static constexpr int RPT = BK / (RW * NWAVE);
+    static_assert(kWave % CPR == 0 && BK % (RW * NWAVE) == 0, "whole windows per stage");
+    static_assert(COLS >= 128, "the row swizzle needs 16 chunks per row");
+    int32_t idx[RPT];
+
+    __device__ __forceinline__ static int window(int i) { return threadIdx.x / kWave + i * NWAVE; }
+    __device__ __forceinline__ static int row_of(int i)
+    {
+        return window(i) * RW + (int)(threadIdx.x % kWave) / CPR;
+    }
+
+    // idxfn(red) -> row index for reduction index red, or -1 for zeros.
+    template <class IdxFn>
+    __device__ __forceinline__ void fetch(int red0, IdxFn idxfn)
+    {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            idx[i] = idxfn(red0 + row_of(i));
+    }
+
+    __device__ __forceinline__ void store(char *) const {}
+
+    // Copy the rows fetched last into the LDS tile; row_bytes is the HBM pitch.
+    __device__ __forceinline__ void load(const u32x4_t &r, char *lds, int col0, int ncols,
+                                         int64_t row_bytes) const
+    {
+        const int pc = (int)(threadIdx.x % kWave) % CPR;
+        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char *)lds);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = row_of(i);
+            const int col = col0 + (pc ^ ((row & 3) << 2)) * 8;
+            const uint32_t voff = (idx[i] >= 0 && col < ncols)
+                                      ? (uint32_t)(idx[i] * row_bytes) + (uint32_t)col * 2
+                                      : kOOB;
+            copy16_to_lds(r, voff, 0,
+                          __builtin_amdgcn_readfirstlane(base + window(i) * (kWave * 16)));
+        }
+    }
+};
+
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // MFMA fragment (8 reduction elements of one column, lane layout of
@@ -398,7 +451,10 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
 #define MOEGG_FWD_DMA 1
 #endif
 #ifndef MOEGG_DX_DMA
-#define MOEGG_DX_DMA 0
+#define MOEGG_DX_DMA 1
+#endif
+#ifndef MOEGG_TILE_DMA
+#define MOEGG_TILE_DMA 1
 #endif
 #ifndef MOEGG_GROUPS_DMA
 #define MOEGG_GROUPS_DMA 1
@@ -726,24 +782,40 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], dy_row);
-        RowTileLoader<C::BN, C::NT> lb;
         const u32x4_t wr =
             rsrc_words(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
         const int N = a.N;
-        auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
-
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        mainloop<C, true, false, true>(
-            st0, st1, nsteps, acc,
-            [&](int s, char *As, char *) {
-                la.load(dyr, As, s * BK, a.N);
-                lb.load(wr, s * BK, k0, a.K, wrowfn);
-            },
-            [&](char *As, char *Bs) {
-                la.store(As);
-                lb.store(Bs);
-            });
+        if constexpr (MOEGG_TILE_DMA != 0) {
+            TileDmaLoader<C::BN, C::NT> lb;
+            auto widx = [=](int n) -> int { return n < N ? n : -1; };
+            lb.fetch(0, widx);
+            mainloop<C, true, false, true>(
+                st0, st1, nsteps, acc,
+                [&](int s, char *As, char *Bs) {
+                    la.load(dyr, As, s * BK, a.N);
+                    lb.load(wr, Bs, k0, a.K, w_row);
+                    lb.fetch((s + 1) * BK, widx);
+                },
+                [&](char *As, char *Bs) {
+                    la.store(As);
+                    lb.store(Bs);
+                });
+        } else {
+            RowTileLoader<C::BN, C::NT> lb;
+            auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
+            mainloop<C, true, false, true>(
+                st0, st1, nsteps, acc,
+                [&](int s, char *As, char *) {
+                    la.load(dyr, As, s * BK, a.N);
+                    lb.load(wr, s * BK, k0, a.K, wrowfn);
+                },
+                [&](char *As, char *Bs) {
+                    la.store(As);
+                    lb.store(Bs);
+                });
+        }
         epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, a.dX, a.K, k0, a.K);
     }
 }
@@ -811,34 +883,65 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         const int32_t *gather = a.gather;
         int32_t *err = a.err;
         const int topk = a.topk;
-        auto dyrowfn = [=](int red) -> uint32_t {
-            if (red >= mc)
-                return kOOB;
-            const int64_t p = start + red;
-            const int q = py ? checked_gather(gather, p, S, err) : (int)p;
-            return q >= 0 ? (uint32_t)(q * dy_row) : kOOB;
-        };
-        auto xrowfn = [=](int red) -> uint32_t {
-            if (red >= mc)
-                return kOOB;
-            const int64_t p = start + red;
-            const int g = px ? checked_gather(gather, p, S, err) : (int)p;
-            return g >= 0 ? (uint32_t)((px ? g / topk : g) * x_row) : kOOB;
-        };
-        RowTileLoader<C::BM, C::NT> la;
-        RowTileLoader<C::BN, C::NT> lb;
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        mainloop<C, true, true, true>(
-            st0, st1, (mc + BK - 1) / BK, acc,
-            [&](int s, char *, char *) {
-                la.load(dyr, s * BK, n0, a.N, dyrowfn);
-                lb.load(xr, s * BK, k0, a.K, xrowfn);
-            },
-            [&](char *As, char *Bs) {
-                la.store(As);
-                lb.store(Bs);
-            });
+        const int nsteps = (mc + BK - 1) / BK;
+        if constexpr (MOEGG_TILE_DMA != 0) {
+            // Row index of reduction index red in dY and in X (-1: zeros).
+            auto dyidx = [=](int red) -> int {
+                if (red >= mc)
+                    return -1;
+                const int64_t p = start + red;
+                return py ? checked_gather(gather, p, S, err) : (int)p;
+            };
+            auto xidx = [=](int red) -> int {
+                if (red >= mc)
+                    return -1;
+                const int64_t p = start + red;
+                const int g = px ? checked_gather(gather, p, S, err) : (int)p;
+                return g < 0 ? -1 : (px ? g / topk : g);
+            };
+            TileDmaLoader<C::BM, C::NT> la;
+            TileDmaLoader<C::BN, C::NT> lb;
+            la.fetch(0, dyidx);
+            lb.fetch(0, xidx);
+            mainloop<C, true, true, true>(
+                st0, st1, nsteps, acc,
+                [&](int s, char *As, char *Bs) {
+                    la.load(dyr, As, n0, a.N, dy_row);
+                    lb.load(xr, Bs, k0, a.K, x_row);
+                    la.fetch((s + 1) * BK, dyidx);
+                    lb.fetch((s + 1) * BK, xidx);
+                },
+                [&](char *, char *) {});
+        } else {
+            auto dyrowfn = [=](int red) -> uint32_t {
+                if (red >= mc)
+                    return kOOB;
+                const int64_t p = start + red;
+                const int q = py ? checked_gather(gather, p, S, err) : (int)p;
+                return q >= 0 ? (uint32_t)(q * dy_row) : kOOB;
+            };
+            auto xrowfn = [=](int red) -> uint32_t {
+                if (red >= mc)
+                    return kOOB;
+                const int64_t p = start + red;
+                const int g = px ? checked_gather(gather, p, S, err) : (int)p;
+                return g >= 0 ? (uint32_t)((px ? g / topk : g) * x_row) : kOOB;
+            };
+            RowTileLoader<C::BM, C::NT> la;
+            RowTileLoader<C::BN, C::NT> lb;
+            mainloop<C, true, true, true>(
+                st0, st1, nsteps, acc,
+                [&](int s, char *, char *) {
+                    la.load(dyr, s * BK, n0, a.N, dyrowfn);
+                    lb.load(xr, s * BK, k0, a.K, xrowfn);
+                },
+                [&](char *As, char *Bs) {
+                    la.store(As);
+                    lb.store(Bs);
+                });
+        }
         if (f32out)
             epilogue_f32<C>(acc, s_dst, reinterpret_cast<float *>(a.dW), a.K, k0, a.K);
         else

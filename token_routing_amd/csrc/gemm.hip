@@ -364,14 +364,18 @@ __device__ __forceinline__ bf16x8_t tr_frag(const char *tile, int kk, int c0)
 // Fragments of one 16-deep step.  A_TR / B_TR: the operand's LDS tile is
 // row-major (reduction rows) and is read with transpose reads; otherwise it
 // is reduction-contiguous (lds_swz layout).
-template <class C, bool A_TR, bool B_TR>
+// ib: number of leading 32-row A blocks holding real rows (PART only; the
+// others are padding of a ragged tail tile and are neither read nor used).
+template <class C, bool A_TR, bool B_TR, bool PART = false>
 __device__ __forceinline__ void read_step(const char *As, const char *Bs, int kk, int wm, int wn,
-                                          bf16x8_t (&a)[C::FM], bf16x8_t (&b)[C::FN])
+                                          bf16x8_t (&a)[C::FM], bf16x8_t (&b)[C::FN], int ib = 0)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int r = lane & 31, chunk = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
+        if (PART && i >= ib)
+            continue;
         if constexpr (A_TR)
             a[i] = tr_frag<C::BM>(As, kk, wm * C::TM + i * 32);
         else
@@ -386,49 +390,53 @@ __device__ __forceinline__ void read_step(const char *As, const char *Bs, int kk
     }
 }
 
-template <class C>
+template <class C, bool PART = false>
 __device__ __forceinline__ void mma_step(const bf16x8_t (&a)[C::FM], const bf16x8_t (&b)[C::FN],
-                                         f32x16_t (&acc)[C::FM][C::FN])
+                                         f32x16_t (&acc)[C::FM][C::FN], int ib = 0)
 {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i) {
+        if (PART && i >= ib)
+            continue;
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
 }
 
 // PIPE = false: each step's reads directly precede its MFMAs (fewer live
-// registers, for kernels that also hold register-staged operands).
-template <class C, bool PIPE, bool A_TR, bool B_TR>
+// registers).  PART: only the first ib 32-row A blocks are computed.
+template <class C, bool PIPE, bool A_TR, bool B_TR, bool PART = false>
 __device__ __forceinline__ void mma_stage(const char *As, const char *Bs,
-                                          f32x16_t (&acc)[C::FM][C::FN], int wm, int wn)
+                                          f32x16_t (&acc)[C::FM][C::FN], int wm, int wn,
+                                          int ib = C::FM)
 {
     if (!PIPE) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             bf16x8_t a[C::FM], b[C::FN];
-            read_step<C, A_TR, B_TR>(As, Bs, kk, wm, wn, a, b);
-            mma_step<C>(a, b, acc);
+            read_step<C, A_TR, B_TR, PART>(As, Bs, kk, wm, wn, a, b, ib);
+            mma_step<C, PART>(a, b, acc, ib);
         }
         return;
     }
     // sched_barrier(0) keeps the compiler from moving the reads back next to
     // their consumers.
     bf16x8_t a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
-    read_step<C, A_TR, B_TR>(As, Bs, 0, wm, wn, a0, b0);
-    read_step<C, A_TR, B_TR>(As, Bs, 1, wm, wn, a1, b1);
+    read_step<C, A_TR, B_TR, PART>(As, Bs, 0, wm, wn, a0, b0, ib);
+    read_step<C, A_TR, B_TR, PART>(As, Bs, 1, wm, wn, a1, b1, ib);
     __builtin_amdgcn_sched_barrier(0);
-    mma_step<C>(a0, b0, acc);
+    mma_step<C, PART>(a0, b0, acc, ib);
     __builtin_amdgcn_sched_barrier(0);
-    read_step<C, A_TR, B_TR>(As, Bs, 2, wm, wn, a0, b0);
+    read_step<C, A_TR, B_TR, PART>(As, Bs, 2, wm, wn, a0, b0, ib);
     __builtin_amdgcn_sched_barrier(0);
-    mma_step<C>(a1, b1, acc);
+    mma_step<C, PART>(a1, b1, acc, ib);
     __builtin_amdgcn_sched_barrier(0);
-    read_step<C, A_TR, B_TR>(As, Bs, 3, wm, wn, a1, b1);
+    read_step<C, A_TR, B_TR, PART>(As, Bs, 3, wm, wn, a1, b1, ib);
     __builtin_amdgcn_sched_barrier(0);
-    mma_step<C>(a0, b0, acc);
+    mma_step<C, PART>(a0, b0, acc, ib);
     __builtin_amdgcn_sched_barrier(0);
-    mma_step<C>(a1, b1, acc);
+    mma_step<C, PART>(a1, b1, acc, ib);
 }
 
 template <class C>
@@ -469,14 +477,11 @@ using RowLoader =
 // for this wave's reads and copies, and barrier.  load(s, As, Bs) starts the
 // reads of stage s; store(As, Bs) writes register-staged data.  The other
 // stage was last read before the previous barrier, so it is free to fill.
-template <class C, bool PIPE, bool A_TR, bool B_TR, class Load, class Store>
-__device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
-                                         f32x16_t (&acc)[C::FM][C::FN], Load load, Store store)
+template <class C, bool PIPE, bool A_TR, bool B_TR, bool PART, class Load, class Store>
+__device__ __forceinline__ void mainloop_body(char *st0, char *st1, int nsteps,
+                                              f32x16_t (&acc)[C::FM][C::FN], Load &load,
+                                              Store &store, int wm, int wn, int ib)
 {
-    const int wave = threadIdx.x / kWave;
-    const int wm = wave / C::WN, wn = wave % C::WN;
-    if (nsteps <= 0)
-        return;
     load(0, st0, st0 + C::A_BYTES);
     store(st0, st0 + C::A_BYTES);
     wait_vmem();
@@ -487,12 +492,32 @@ __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
         const bool more = s + 1 < nsteps;
         if (more)
             load(s + 1, nxt, nxt + C::A_BYTES);
-        mma_stage<C, PIPE, A_TR, B_TR>(cur, cur + C::A_BYTES, acc, wm, wn);
+        mma_stage<C, PIPE, A_TR, B_TR, PART>(cur, cur + C::A_BYTES, acc, wm, wn, ib);
         if (more)
             store(nxt, nxt + C::A_BYTES);
         wait_vmem();
         __syncthreads();
     }
+}
+
+// rows: tile rows (A side) holding real data.  A wave whose 32-row blocks
+// are all real runs the branch-free body; a wave of a ragged tail tile skips
+// the MFMAs and A reads of its padding blocks (the barriers are the same).
+template <class C, bool PIPE, bool A_TR, bool B_TR, class Load, class Store>
+__device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
+                                         f32x16_t (&acc)[C::FM][C::FN], Load load, Store store,
+                                         int rows = C::BM)
+{
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    if (nsteps <= 0)
+        return;
+    const int ib = __builtin_amdgcn_readfirstlane(
+        min(C::FM, max(0, (rows - wm * C::TM + 31) / 32)));
+    if (ib == C::FM)
+        mainloop_body<C, PIPE, A_TR, B_TR, false>(st0, st1, nsteps, acc, load, store, wm, wn, ib);
+    else
+        mainloop_body<C, PIPE, A_TR, B_TR, true>(st0, st1, nsteps, acc, load, store, wm, wn, ib);
 }
 
 // Row and column of accumulator element r of 32x32 block (i, j) for this lane.
@@ -724,7 +749,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             [&](char *As, char *Bs) {
                 la.store(As);
                 lb.store(Bs);
-            });
+            },
+            rows);
         epilogue_bf16<C>(st0, st1, acc, s_dst, s_scale, fm, a.Y, a.N, n0, a.N);
     }
 }
@@ -801,7 +827,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                 [&](char *As, char *Bs) {
                     la.store(As);
                     lb.store(Bs);
-                });
+                },
+            rows);
         } else {
             RowTileLoader<C::BN, C::NT> lb;
             auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
@@ -814,7 +841,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                 [&](char *As, char *Bs) {
                     la.store(As);
                     lb.store(Bs);
-                });
+                },
+            rows);
         }
         epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, a.dX, a.K, k0, a.K);
     }
@@ -913,7 +941,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
                     la.fetch((s + 1) * BK, dyidx);
                     lb.fetch((s + 1) * BK, xidx);
                 },
-                [&](char *, char *) {});
+                [&](char *, char *) {},
+            min(C::BM, a.N - n0));
         } else {
             auto dyrowfn = [=](int red) -> uint32_t {
                 if (red >= mc)
@@ -940,7 +969,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
                 [&](char *As, char *Bs) {
                     la.store(As);
                     lb.store(Bs);
-                });
+                },
+            min(C::BM, a.N - n0));
         }
         if (f32out)
             epilogue_f32<C>(acc, s_dst, reinterpret_cast<float *>(a.dW), a.K, k0, a.K);
@@ -1014,7 +1044,8 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
                 [&](char *As, char *Bs) {
                     la.store(As);
                     lb.store(Bs);
-                });
+                },
+            min(C::BM, g.m - m0));
         } else {
             RowTileLoader<C::BN, C::NT> lb;
             auto wrowfn = [=](int red) -> uint32_t {
@@ -1030,7 +1061,8 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
                 [&](char *As, char *Bs) {
                 la.store(As);
                 lb.store(Bs);
-            });
+            },
+            min(C::BM, g.m - m0));
         }
         epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, static_cast<char *>(g.y), g.ldy, n0,
                          g.n);

@@ -99,24 +99,50 @@ __global__ __launch_bounds__(kScanThreads) void route_scan(int32_t *counts, int 
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     constexpr int kWaves = kScanThreads / kWave;
-    for (int e = wave; e < E; e += kWaves) {
-        int32_t *row = counts + (int64_t)e * nchunks;
-        int carry = 0;
-        for (int c0 = 0; c0 < nchunks; c0 += kWave) {
-            const int c = c0 + lane;
-            const int v = c < nchunks ? row[c] : 0;
-            int incl = v;
-            for (int d = 1; d < kWave; d <<= 1) {
-                int u = __shfl_up(incl, d, kWave);
-                if (lane >= d)
-                    incl += u;
+    // Each wave scans kRows experts' chunk rows at a time; a lane owns 4
+    // consecutive chunks of each row.  All loads of a batch are issued
+    // before any is used, so a batch costs one memory round trip.
+    constexpr int kRows = 4, kPer = 4;
+    for (int e0 = wave * kRows; e0 < E; e0 += kWaves * kRows) {
+        int carry[kRows] = {0, 0, 0, 0};
+        for (int c0 = 0; c0 < nchunks; c0 += kWave * kPer) {
+            int v[kRows][kPer];
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+#pragma unroll
+                for (int q = 0; q < kPer; ++q) {
+                    const int e = e0 + r, c = c0 + lane * kPer + q;
+                    v[r][q] = (e < E && c < nchunks) ? counts[(int64_t)e * nchunks + c] : 0;
+                }
+#pragma unroll
+            for (int r = 0; r < kRows; ++r) {
+                int local = 0;
+#pragma unroll
+                for (int q = 0; q < kPer; ++q)
+                    local += v[r][q];
+                int incl = local;
+                for (int d = 1; d < kWave; d <<= 1) {
+                    const int u = __shfl_up(incl, d, kWave);
+                    if (lane >= d)
+                        incl += u;
+                }
+                int run = carry[r] + incl - local;
+                const int e = e0 + r;
+#pragma unroll
+                for (int q = 0; q < kPer; ++q) {
+                    const int c = c0 + lane * kPer + q;
+                    if (e < E && c < nchunks)
+                        counts[(int64_t)e * nchunks + c] = run;
+                    run += v[r][q];
+                }
+                carry[r] += __shfl(incl, kWave - 1, kWave);
             }
-            if (c < nchunks)
-                row[c] = carry + incl - v;
-            carry += __shfl(incl, kWave - 1, kWave);
         }
         if (lane == 0)
-            tot[e] = carry;
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+                if (e0 + r < E)
+                    tot[e0 + r] = carry[r];
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kScanThreads) {

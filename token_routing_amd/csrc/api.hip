@@ -262,6 +262,7 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     p.N = N;
     p.K = K;
     p.flags = flags;
+    p.topk_div = moegg::make_fastdiv((uint32_t)topk);
     return from_hip(moegg::dw_launch(p, cus, static_cast<hipStream_t>(stream)));
 }
 

@@ -281,9 +281,15 @@ struct RowTileLoader {
 // The same row-major tile, copied HBM -> LDS without registers.  A wave's
 // 1 KiB window is RW = 64 / (COLS / 8) whole rows; lane l writes physical
 // chunk l % (COLS / 8) of window row l / (COLS / 8) and therefore fetches the
-// logical chunk that the row swizzle maps there.  Row indices for the next
-// stage are fetched one stage ahead (fetch), so a gathered row index (one
-// global load) is in registers before its row is copied (load).
+// logical chunk that the row swizzle maps there.
+//
+// Row indices are three-phase: fetch(red0, raw) only issues the loads of the
+// next stage's raw row indices (e.g. gather entries) into registers; at the
+// next stage, prepare(…, fin) turns them into byte offsets and issue() starts
+// the copies.  The raw values are consumed a whole stage after they were
+// requested, and every prepare of a stage runs before its first copy is
+// issued: the compiler (which does not see the copies) may insert a wait for
+// the raw loads there, and at that point nothing else is in flight.
 template <int COLS, int NT>
 struct TileDmaLoader {
     static constexpr int CPR = COLS / 8;
@@ -292,7 +298,8 @@ struct TileDmaLoader {
     static constexpr int RPT = BK / (RW * NWAVE);
     static_assert(kWave % CPR == 0 && BK % (RW * NWAVE) == 0, "whole windows per stage");
     static_assert(COLS >= 128, "the row swizzle needs 16 chunks per row");
-    int32_t idx[RPT];
+    int32_t raw[RPT];
+    int red0 = 0;
 
     __device__ __forceinline__ static int window(int i) { return threadIdx.x / kWave + i * NWAVE; }
     __device__ __forceinline__ static int row_of(int i)
@@ -300,35 +307,49 @@ struct TileDmaLoader {
         return window(i) * RW + (int)(threadIdx.x % kWave) / CPR;
     }
 
-    // idxfn(red) -> row index for reduction index red, or -1 for zeros.
-    template <class IdxFn>
-    __device__ __forceinline__ void fetch(int red0, IdxFn idxfn)
+    // rawfn(red) -> the raw row index of reduction index red (a load or a
+    // plain value; must stay in bounds for any red).
+    template <class RawFn>
+    __device__ __forceinline__ void fetch(int red_base, RawFn rawfn)
     {
+        red0 = red_base;
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-            idx[i] = idxfn(red0 + row_of(i));
+            raw[i] = rawfn(red_base + row_of(i));
     }
 
     __device__ __forceinline__ void store(char *) const {}
 
-    // Copy the rows fetched last into the LDS tile; row_bytes is the HBM pitch.
-    __device__ __forceinline__ void load(const u32x4_t &r, char *lds, int col0, int ncols,
-                                         int64_t row_bytes) const
+    // Turn the raw indices fetched last into byte offsets: fin(red, raw) ->
+    // HBM row (-1: zeros); row_bytes is the HBM pitch.  Call before issuing
+    // any copy of the stage (see mainloop_load below).
+    template <class FinFn>
+    __device__ __forceinline__ void prepare(int col0, int ncols, int64_t row_bytes, FinFn fin)
     {
         const int pc = (int)(threadIdx.x % kWave) % CPR;
-        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(
-            (__attribute__((address_space(3))) char *)lds);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int row = row_of(i);
+            const int idx = fin(red0 + row, raw[i]);
             const int col = col0 + (pc ^ ((row & 3) << 2)) * 8;
-            const uint32_t voff = (idx[i] >= 0 && col < ncols)
-                                      ? (uint32_t)(idx[i] * row_bytes) + (uint32_t)col * 2
-                                      : kOOB;
-            copy16_to_lds(r, voff, 0,
-                          __builtin_amdgcn_readfirstlane(base + window(i) * (kWave * 16)));
+            voff[i] = (idx >= 0 && col < ncols)
+                          ? (uint32_t)idx * (uint32_t)row_bytes + (uint32_t)col * 2
+                          : kOOB;
         }
     }
+
+    // Copy the prepared rows into the LDS tile.
+    __device__ __forceinline__ void issue(const u32x4_t &r, char *lds) const
+    {
+        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) char *)lds);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            copy16_to_lds(r, voff[i], 0,
+                          __builtin_amdgcn_readfirstlane(base + window(i) * (kWave * 16)));
+    }
+
+    uint32_t voff[RPT];
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -815,14 +836,17 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         zero_acc<C>(acc);
         if constexpr (MOEGG_TILE_DMA != 0) {
             TileDmaLoader<C::BN, C::NT> lb;
-            auto widx = [=](int n) -> int { return n < N ? n : -1; };
-            lb.fetch(0, widx);
+            auto wraw = [](int n) -> int { return n; };
+            auto wfin = [=](int n, int) -> int { return n < N ? n : -1; };
+            lb.fetch(0, wraw);
             mainloop<C, true, false, true>(
                 st0, st1, nsteps, acc,
                 [&](int s, char *As, char *Bs) {
+                    lb.prepare(k0, a.K, w_row, wfin);
+                    __builtin_amdgcn_sched_barrier(0);
                     la.load(dyr, As, s * BK, a.N);
-                    lb.load(wr, Bs, k0, a.K, w_row);
-                    lb.fetch((s + 1) * BK, widx);
+                    lb.issue(wr, Bs);
+                    lb.fetch((s + 1) * BK, wraw);
                 },
                 [&](char *As, char *Bs) {
                     la.store(As);
@@ -854,7 +878,14 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 
 constexpr int kGroupK = 8;
 
-template <class C>
+__device__ __forceinline__ int fast_div(uint32_t n, FastDiv d)
+{
+    return (int)((__umulhi(n, d.mul) + n) >> d.shift);
+}
+
+// PX / PY: the forward's permute flags, as template parameters so that the
+// per-stage row-index code has no flag branches.
+template <class C, bool PX, bool PY>
 __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
 {
     __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
@@ -865,7 +896,6 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
     __shared__ int s_dst[C::BM];
     __shared__ int s_scratch[2];
 
-    const bool px = a.flags & MOEGG_PERMUTE_X, py = a.flags & MOEGG_PERMUTE_Y;
     const bool f32out = a.flags & MOEGG_DW_FP32_OUT;
     const int ntn = (a.N + C::BM - 1) / C::BM, ntk = (a.K + C::BN - 1) / C::BN;
     const int per_expert = ntn * ntk;
@@ -884,7 +914,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
     __syncthreads();
     const int total = a.E * per_expert;
     const int64_t dy_row = (int64_t)a.N * 2, x_row = (int64_t)a.K * 2;
-    const int64_t x_rows = px ? a.S / a.topk : a.S;
+    const int64_t x_rows = PX ? a.S / a.topk : a.S;
     const u32x4_t dyr = rsrc_words(a.dY, a.S * dy_row);
     const u32x4_t xr = rsrc_words(a.X, x_rows * x_row);
 
@@ -915,35 +945,66 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         zero_acc<C>(acc);
         const int nsteps = (mc + BK - 1) / BK;
         if constexpr (MOEGG_TILE_DMA != 0) {
-            // Row index of reduction index red in dY and in X (-1: zeros).
-            auto dyidx = [=](int red) -> int {
-                if (red >= mc)
-                    return -1;
-                const int64_t p = start + red;
-                return py ? checked_gather(gather, p, S, err) : (int)p;
+            // Row index of reduction index red in dY and in X (-1: zeros),
+            // without branches.  raw: the gather entry (read clamped into the
+            // expert's rows) or the sorted position; fin: validity and, for
+            // X under permute_x, the token row g / topk.  A gather entry
+            // outside [0, S) gives zeros and is reported once per tile.
+            const FastDiv tdiv = a.topk_div;
+            const uint32_t Su = (uint32_t)S;
+            bool bad = false;
+            auto graw = [=](int red) -> int {
+                const int64_t p = start + min(red, mc - 1);
+                if constexpr (PX || PY)
+                    return gather[p];
+                return (int)p;
             };
-            auto xidx = [=](int red) -> int {
-                if (red >= mc)
-                    return -1;
-                const int64_t p = start + red;
-                const int g = px ? checked_gather(gather, p, S, err) : (int)p;
-                return g < 0 ? -1 : (px ? g / topk : g);
+            auto pos = [=](int red) -> int { return start + red; };
+            auto dyfin = [&](int red, int g) -> int {
+                const bool ok = !PY || (uint32_t)g < Su;
+                bad |= red < mc && !ok;
+                return (red < mc && ok) ? (PY ? g : start + red) : -1;
+            };
+            auto xfin = [&](int red, int g) -> int {
+                const bool ok = !PX || (uint32_t)g < Su;
+                bad |= red < mc && !ok;
+                return (red < mc && ok) ? (PX ? fast_div((uint32_t)g, tdiv) : start + red) : -1;
             };
             TileDmaLoader<C::BM, C::NT> la;
             TileDmaLoader<C::BN, C::NT> lb;
-            la.fetch(0, dyidx);
-            lb.fetch(0, xidx);
-            mainloop<C, true, true, true>(
-                st0, st1, nsteps, acc,
-                [&](int s, char *As, char *Bs) {
-                    la.load(dyr, As, n0, a.N, dy_row);
-                    lb.load(xr, Bs, k0, a.K, x_row);
-                    la.fetch((s + 1) * BK, dyidx);
-                    lb.fetch((s + 1) * BK, xidx);
-                },
-                [&](char *, char *) {},
-            min(C::BM, a.N - n0));
+            if (nsteps > 0) {
+                if constexpr (PY)
+                    la.fetch(0, graw);
+                else
+                    la.fetch(0, pos);
+                if constexpr (PX)
+                    lb.fetch(0, graw);
+                else
+                    lb.fetch(0, pos);
+                mainloop<C, true, true, true>(
+                    st0, st1, nsteps, acc,
+                    [&](int s, char *As, char *Bs) {
+                        la.prepare(n0, a.N, dy_row, dyfin);
+                        lb.prepare(k0, a.K, x_row, xfin);
+                        __builtin_amdgcn_sched_barrier(0);
+                        la.issue(dyr, As);
+                        lb.issue(xr, Bs);
+                        if constexpr (PY)
+                            la.fetch((s + 1) * BK, graw);
+                        else
+                            la.fetch((s + 1) * BK, pos);
+                        if constexpr (PX)
+                            lb.fetch((s + 1) * BK, graw);
+                        else
+                            lb.fetch((s + 1) * BK, pos);
+                    },
+                    [&](char *, char *) {},
+                    min(C::BM, a.N - n0));
+            }
+            if (bad)
+                raise_error(err, kErrGather);
         } else {
+            const bool px = PX, py = PY;
             auto dyrowfn = [=](int red) -> uint32_t {
                 if (red >= mc)
                     return kOOB;
@@ -1096,7 +1157,9 @@ using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
 template __global__ void fwd_kernel<BigCfg>(FwdParams);
 template __global__ void fwd_kernel<SmallCfg>(FwdParams);
 template __global__ void dx_kernel<DxCfg>(DxParams);
-template __global__ void dw_kernel<DwCfg>(DwParams);
+template __global__ void dw_kernel<DwCfg, false, false>(DwParams);
+template __global__ void dw_kernel<DwCfg, true, false>(DwParams);
+template __global__ void dw_kernel<DwCfg, false, true>(DwParams);
 template __global__ void groups_kernel<GroupCfg, true>(GroupsParams);
 template __global__ void groups_kernel<GroupCfg, false>(GroupsParams);
 
@@ -1150,13 +1213,25 @@ hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
+template <bool PX, bool PY>
+static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 {
     using C = DwCfg;
     const int64_t tiles =
         (int64_t)p.E * ((p.N + C::BM - 1) / C::BM) * ((p.K + C::BN - 1) / C::BN);
-    static int res = resident_blocks(dw_kernel<C>, C::NT);
-    hipLaunchKernelGGL(dw_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    static int res = resident_blocks(dw_kernel<C, PX, PY>, C::NT);
+    hipLaunchKernelGGL((dw_kernel<C, PX, PY>), dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0,
+                       stream, p);
+}
+
+hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
+{
+    if (p.flags & MOEGG_PERMUTE_X)
+        dw_launch_flags<true, false>(p, cus, stream);
+    else if (p.flags & MOEGG_PERMUTE_Y)
+        dw_launch_flags<false, true>(p, cus, stream);
+    else
+        dw_launch_flags<false, false>(p, cus, stream);
     return hipGetLastError();
 }
 

@@ -35,6 +35,22 @@ struct DxParams {
     uint32_t flags;
 };
 
+// n / d for 0 <= n < 2^31 as (umulhi(n, mul) + n) >> shift, d >= 1.
+struct FastDiv {
+    uint32_t mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d)
+        ++l;
+    FastDiv f;
+    f.mul = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    f.shift = l;
+    return f;
+}
+
 // dW_e = dY_e^T X_e.
 struct DwParams {
     const char *X;
@@ -46,6 +62,7 @@ struct DwParams {
     int64_t S;
     int topk, E, N, K;
     uint32_t flags;
+    FastDiv topk_div;
 };
 
 // Explicit groups (passed by value in the kernel arguments).

@@ -204,35 +204,52 @@ def measured_traffic(workload, label):
 
 
 def cpu_baseline(st, budget_s):
-    """The CPU oracle on a bounded sample of the workload (single thread)."""
+    """The CPU oracle on a bounded sample of the workload (one thread).
+
+    The forward of a few output rows is timed once to size the sample to about
+    budget_s seconds, then that many random output rows (all columns) are
+    computed; the rate is useful FLOPs of the sampled rows per second.
+    """
     import oracle
 
     wl = st.inputs
-    t0 = time.perf_counter()
-    done_flops = 0.0
     if st.name == "dual":
         x, w = wl.groups[0]
-        rows = 64
+        per_row = 2.0 * x.shape[1] * w.shape[1]
+        t0 = time.perf_counter()
+        oracle.dense_gemm_kn(synth.bits(x[:4]), synth.bits(w))
+        rows = max(4, min(x.shape[0], int(budget_s / max(time.perf_counter() - t0, 1e-6) * 4)))
+        t0 = time.perf_counter()
         oracle.dense_gemm_kn(synth.bits(x[:rows]), synth.bits(w))
-        done_flops = 2.0 * rows * x.shape[1] * w.shape[1]
-        sample = f"group 0, first {rows} rows"
-    else:
-        ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, BLOCK_M)
-        E, N, K = wl.W.shape
-        Xb, Wb = synth.bits(wl.X), synth.bits(wl.W)
-        rng = np.random.default_rng(0)
-        per_row = 2.0 * N * K
-        nrows = max(1, int(budget_s * 1.0e9 / per_row))   # ~1 GFLOP/s plain loops
+        dt = time.perf_counter() - t0
+        return {"value": per_row * rows / dt / 1e12, "unit": "TFLOP/s", "cores": 1,
+                "kind": "oracle", "sample": f"group 0, first {rows} rows x all columns",
+                "seconds": round(dt, 3)}
+    E, N, K = wl.W.shape
+    ids = wl.ids.numpy().reshape(-1)
+    Xb, Wb = synth.bits(wl.X), synth.bits(wl.W)
+    gate = wl.weights.numpy().reshape(-1)
+    t0 = time.perf_counter()
+    ref_route = oracle.route(ids, wl.E, BLOCK_M)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    per_row = 2.0 * N * K
+
+    def run(nrows):
         rows = rng.choice(wl.S, size=min(nrows, wl.S), replace=False)
         if wl.flags & synth.PERMUTE_Y:
-            rows = ref_route["gather"][rows]
-        oracle.grouped_gemm_fwd(Xb, Wb, ref_route["m_sizes"], ref_route["gather"],
-                                wl.weights.numpy().reshape(-1), wl.topk, wl.flags, rows=rows)
-        done_flops = per_row * len(rows)
-        sample = f"route (all {wl.S} slots) + forward of {len(rows)} random output rows x all {N} columns"
-    dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+            rows = ref_route["gather"][rows]     # output rows are slots
+        t = time.perf_counter()
+        oracle.grouped_gemm_fwd(Xb, Wb, ref_route["m_sizes"], ref_route["gather"], gate,
+                                wl.topk, wl.flags, rows=rows)
+        return len(rows), time.perf_counter() - t
+
+    n1, t1 = run(2)
+    n, dt = run(max(1, int(budget_s / max(t1 / n1, 1e-9))))
+    return {"value": per_row * n / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"routing of all {wl.S} slots ({t_route:.3f} s) + forward of {n} random "
+                      f"output rows x all {N} columns (K={K}); the oracle's rate on them",
+            "seconds": round(dt, 3)}
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -248,6 +265,84 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     return 0
 
 
+KERNEL_LABELS = (("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
+                 ("groups_kernel", "groups"), ("route_count", "route_count"),
+                 ("route_scan", "route_scan"), ("route_scatter", "route_scatter"))
+
+
+def _label(kernel_name):
+    for key, lab in KERNEL_LABELS:
+        if key in kernel_name:
+            return lab
+    return None
+
+
+def _counter_means(path, counter):
+    """Mean counter value (KiB for FETCH_SIZE / WRITE_SIZE) per kernel label."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        lab = _label(r["Kernel_Name"])
+        if lab is None and "elementwise" in r["Kernel_Name"]:
+            lab = "copy"
+        if lab:
+            acc.setdefault(lab, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize(prof_dir, workload, command):
+    """Turn rocprofv3 CSV output under prof_dir (trace/, fetch/, write/,
+    copy_FETCH_SIZE/, copy_WRITE_SIZE/) into profiles/ summaries: the kernel
+    statistics table and, per GEMM kernel, calibrated HBM bytes per launch."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(prof_dir, "trace", "*kernel_stats.csv"))[0]
+    rows = list(csv.DictReader(open(stats)))
+    fetch = _counter_means(glob.glob(os.path.join(prof_dir, "fetch", "*counter_collection.csv"))[0],
+                           "FETCH_SIZE")
+    write = _counter_means(glob.glob(os.path.join(prof_dir, "write", "*counter_collection.csv"))[0],
+                           "WRITE_SIZE")
+    cal = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        f = glob.glob(os.path.join(prof_dir, f"copy_{c}", "*counter_collection.csv"))[0]
+        import csv as _csv
+        vals = sorted(float(r["Counter_Value"]) for r in _csv.DictReader(open(f))
+                      if r["Counter_Name"] == c)
+        cal[c] = (1 << 30) / 1024.0 / vals[len(vals) // 2]   # true KiB per counter KiB (median launch)
+    sha = kernel_source_sha()
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = [f"# rocprofv3 kernel statistics: {workload}", "",
+             f"Workload: {WORKLOAD_DESC[workload]}", "",
+             "Commands (from the repository root on the GPU box):", "",
+             "```", *command.strip().splitlines(), "```", "",
+             f"Kernel sources sha256[:16]: `{sha}`", "",
+             "| kernel | calls | average ns | total % |", "|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    lines += ["", "HBM traffic per launch (FETCH_SIZE x {:.3f}, WRITE_SIZE x {:.3f}; factors from a "
+              "1 GiB device copy read by the same counters):".format(cal["FETCH_SIZE"],
+                                                                  cal["WRITE_SIZE"]), "",
+              "| kernel | read MB | written MB |", "|---|---|---|"]
+    for lab in ("fwd", "dX", "dW", "groups"):
+        if lab in fetch and lab in write:
+            rd = fetch[lab] * 1024 * cal["FETCH_SIZE"]
+            wr = write[lab] * 1024 * cal["WRITE_SIZE"]
+            lines.append(f"| {lab} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
+            json.dump({"kernel_src_sha": sha, "workload": workload, "kernel": lab,
+                       "bytes_per_launch": round(rd + wr), "read_bytes": round(rd),
+                       "write_bytes": round(wr), "fetch_scale": cal["FETCH_SIZE"],
+                       "write_scale": cal["WRITE_SIZE"]},
+                      open(os.path.join(ROOT, "profiles", f"traffic_{lab}_{workload}.json"), "w"),
+                      indent=1)
+    out = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print(out)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,7 +353,13 @@ def main():
                     help="seconds of CPU oracle work for the baseline (0 disables)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize", metavar="PROF_DIR",
+                    help="write profiles/ summaries from rocprofv3 CSVs (no GPU needed)")
+    ap.add_argument("--command-file", help="text of the profiling commands, for --summarize")
     args = ap.parse_args()
+    if args.summarize:
+        cmd = open(args.command_file).read() if args.command_file else "(not recorded)"
+        return summarize(args.summarize, args.workload, cmd)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path is not sharded "
               "across GPUs", file=sys.stderr)

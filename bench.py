@@ -131,7 +131,7 @@ def build_dual_step(wl):
 
 def make_step(name):
     if name == "mixtral":
-        return build_layer_step(synth.mixtral(), dY_seed=2003)
+        return build_layer_step(synth.mixtral(), dY_seed=synth.SEEDS["mixtral_bwd_dy"])
     if name == "fine":
         return build_layer_step(synth.fine_bwd(), dY_seed=synth.SEEDS["fine_bwd_dy"])
     if name == "fine_fwd":

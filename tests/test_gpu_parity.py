@@ -228,16 +228,16 @@ def _bwd_case(mg, wl, flags, dw_flags_extra=0, rows_dx=None, rows_dw=None, cols_
     ref_dw = oracle.grouped_gemm_dW(synth.bits(wl.X), synth.bits(wl.dY), ref_route["m_sizes"],
                                     ref_route["gather"], wl.topk, flags, E, rows=rows_dw,
                                     cols=cols_dw)
-    got_dx = dX.float().cpu().numpy()
-    got_dw = dW.float().reshape(E * N, K).cpu().numpy()
-    if rows_dx is not None:
-        got_dx = got_dx[rows_dx]
-    if cols_dx is not None:
-        got_dx = got_dx[:, cols_dx]
-    if rows_dw is not None:
-        got_dw = got_dw[rows_dw]
-    if cols_dw is not None:
-        got_dw = got_dw[:, cols_dw]
+    def pick(t, rows, cols):
+        # select on the device: a full-size dW is 1.9 GB
+        if rows is not None:
+            t = t[torch.as_tensor(rows, dtype=torch.long, device=t.device)]
+        if cols is not None:
+            t = t[:, torch.as_tensor(cols, dtype=torch.long, device=t.device)]
+        return t.float().cpu().numpy()
+
+    got_dx = pick(dX, rows_dx, cols_dx)
+    got_dw = pick(dW.reshape(E * N, K), rows_dw, cols_dw)
     return got_dx, ref_dx, got_dw, ref_dw, dW, ref_route
 
 
@@ -258,6 +258,40 @@ def test_bwd_small(mg, flags, case):
     _assert_close(gdw, rdw, f"dW {case} flags={flags}")
     for e in empty:
         assert torch.count_nonzero(dW[e]).item() == 0
+
+
+# dX over a long reduction (N >= 8192) runs the four-wave engine: N = 8200
+# leaves a ragged last 32-row slot, K = 520 a ragged last column tile.
+BWD_LONG_N = [(150, 520, 8200, 5, 2, 14, (2,))]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])
+@pytest.mark.parametrize("case", BWD_LONG_N, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in BWD_LONG_N])
+def test_bwd_long_reduction(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty, with_dy=True)
+    gdx, rdx, gdw, rdw, dW, _ = _bwd_case(mg, wl, flags)
+    _assert_close(gdx, rdx, f"dX {case} flags={flags}")
+    _assert_close(gdw, rdw, f"dW {case} flags={flags}")
+    for e in empty:
+        assert torch.count_nonzero(dW[e]).item() == 0
+
+
+def test_bwd_mixtral_sampled(mg):
+    wl = synth.mixtral()
+    wl.dY = synth.normal_bf16((wl.S, wl.N), 0.01, synth.generator(synth.SEEDS["mixtral_bwd_dy"]))
+    rng = np.random.default_rng(3)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    rows_dx = _sample_rows(ref_route["offsets"], 256, 16, rng, wl.S)
+    cols_dx = _sample_cols(wl.K, 256, 24, rng)
+    E, N, K = wl.W.shape
+    rows_dw = np.array(sorted({e * N + n for e in range(E) for n in [0, 255, 256, N - 1]
+                               + rng.integers(0, N, 3).tolist()}))
+    cols_dw = _sample_cols(K, 256, 16, rng)
+    gdx, rdx, gdw, rdw, _, _ = _bwd_case(mg, wl, wl.flags, rows_dx=rows_dx, rows_dw=rows_dw,
+                                         cols_dx=cols_dx, cols_dw=cols_dw)
+    _assert_close(gdx, rdx, "dX mixtral sampled")
+    _assert_close(gdw, rdw, "dW mixtral sampled")
 
 
 def test_dw_fp32_out(mg):

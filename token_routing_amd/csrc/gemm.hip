@@ -541,6 +541,386 @@ __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
         mainloop_body<C, PIPE, A_TR, B_TR, true>(st0, st1, nsteps, acc, load, store, wm, wn, ib);
 }
 
+// ---------------------------------------------------------------------------
+// 32-deep LDS slots and explicit waits
+// ---------------------------------------------------------------------------
+
+constexpr int SK = 32;        // reduction elements per slot
+constexpr int kSlots = 4;
+
+// 64-byte slot rows: 16 rows read at one logical chunk land in 16 distinct
+// 16-byte bank groups of a 256-byte bank window (4 rows per window, the
+// chunk XOR-ed with (row / 4) % 4).
+__device__ __forceinline__ int slot_off(int row, int chunk)
+{
+    return row * (SK * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ void wg_barrier()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void wait_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One wave's share of one operand of a slot: NC windows of 16 rows x 64
+// bytes.  Lane l writes window row l / 4 at physical chunk l % 4 and so
+// fetches the logical chunk that slot_off maps there.
+template <int NC>
+struct SlotCopier {
+    uint32_t off[NC];  // HBM byte offset of this lane's row + chunk (kOOB: zero row)
+    int kc;            // reduction offset of this lane's chunk within a slot
+    uint32_t lds0;     // LDS address of the wave's first window in slot 0
+
+    __device__ __forceinline__ static int lane() { return threadIdx.x & (kWave - 1); }
+    // Tile row of window j for this lane (first_row: the wave's first row).
+    __device__ __forceinline__ static int row(int first_row, int j)
+    {
+        return first_row + 16 * j + (lane() >> 2);
+    }
+    __device__ __forceinline__ void init(char *slot0_part, int first_row)
+    {
+        const int lc = (lane() & 3) ^ ((lane() >> 4) & 3);
+        kc = lc * 8;
+        lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(
+                   (__attribute__((address_space(3))) char *)slot0_part)) +
+               first_row * (SK * 2);
+    }
+    __device__ __forceinline__ void set_row(int j, int64_t hbm_row, int64_t row_bytes)
+    {
+        off[j] = hbm_row < 0 ? kOOB : (uint32_t)(hbm_row * row_bytes) + (uint32_t)kc * 2;
+    }
+    // Copy j of reduction elements [k0, k0 + 32) into slot buffer `slot`.
+    template <int SLOT_BYTES>
+    __device__ __forceinline__ void issue_one(const u32x4_t &r, int j, int slot, int k0,
+                                              int klen) const
+    {
+        copy16_to_lds(r, k0 + kc < klen ? off[j] : kOOB, (uint32_t)k0 * 2,
+                      lds0 + (uint32_t)(slot * SLOT_BYTES + j * kWave * 16));
+    }
+    // Copies of reduction elements [k0, k0 + 32) into slot buffer `slot`.
+    template <int SLOT_BYTES>
+    __device__ __forceinline__ void issue(const u32x4_t &r, int slot, int k0, int klen) const
+    {
+        const bool kin = k0 + kc < klen;
+#pragma unroll
+        for (int j = 0; j < NC; ++j)
+            copy16_to_lds(r, kin ? off[j] : kOOB, (uint32_t)k0 * 2,
+                          lds0 + (uint32_t)(slot * SLOT_BYTES + j * kWave * 16));
+    }
+};
+
+// Fragments of 16-deep step kk (0 or 1) of a slot.
+template <class C, bool PART>
+__device__ __forceinline__ void read_slot_step(const char *As, const char *Bs, int kk, int wm,
+                                               int wn, bf16x8_t (&a)[C::FM],
+                                               bf16x8_t (&b)[C::FN], int ib)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 31, chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        if (PART && i >= ib)
+            continue;
+        a[i] = *reinterpret_cast<const bf16x8_t *>(As + slot_off(wm * C::TM + i * 32 + r, chunk));
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t *>(Bs + slot_off(wn * C::TN + j * 32 + r, chunk));
+}
+
+// Wait for the copy batch `newer` batches older than the newest (each batch
+// is NC copies of this wave).
+template <int NC>
+__device__ __forceinline__ void wait_batch(int newer)
+{
+    if (newer >= 2)
+        wait_vmcnt<2 * NC>();
+    else if (newer == 1)
+        wait_vmcnt<NC>();
+    else
+        wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
+// Four-wave engine: one wave per SIMD, 128 x 128 outputs per wave
+// ---------------------------------------------------------------------------
+//
+// LDS read bandwidth (about 128 bytes per clock per CU) is what bounds a
+// bf16 MFMA tile on this chip.  A wave computing FM x FN blocks of 32 x 32
+// reads FM + FN fragments of 1 KiB per 16-deep step for FM * FN MFMAs, so a
+// 128 x 128 wave tile (4 x 4) needs 0.5 KiB of LDS reads per MFMA against
+// 0.75 KiB for 128 x 64.  With 256 accumulators per wave that allows one
+// wave per SIMD: four waves cover a 256 x 256 tile.
+//
+// The wave hides latency by itself: every MFMA of a 16-deep step is followed
+// by one memory operation, reads of the next step's fragments or HBM -> LDS
+// copies, in a fixed order (sched_barrier pins it).  LDS holds four 32-deep
+// slots (A then B, 64-byte rows, slot_off layout).  Per slot q:
+//
+//   phase A: MFMAs of step 0 (fragments F0)  |  reads of step 1 -> F1, then
+//            half of this wave's copies of slot q + 3 (into the buffer of q - 1)
+//   wait: own LDS reads, own copies of slot q + 1; barrier
+//   phase B: MFMAs of step 1 (F1)            |  reads of slot q + 1 step 0 -> F0,
+//            then the other half of the copies
+//
+// Before the barrier of slot q every wave has finished all its reads of
+// slot q - 1 (its last ones were in phase A of q - 1 and were waited for at
+// that slot's barrier), so after it the buffer can take copies; and every
+// wave's copies of slot q + 1 have landed, so phase B may read it.  Copies
+// get one and a half to two slots (1500-2000 MFMA cycles) to arrive, and the
+// address unit sees four per wave per phase.
+
+template <class C>
+struct Quad {
+    static_assert(C::WM == 2 && C::WN == 2 && C::FM == 4 && C::FN == 4,
+                  "2 x 2 waves of 4 x 4 blocks");
+    static constexpr int A = C::BM * SK * 2, B = C::BN * SK * 2, SLOT = A + B;
+    static constexpr int NCA = C::BM / 64, NCB = C::BN / 64;  // copies per wave and slot
+    static constexpr int NCOPY = NCA + NCB;
+    static_assert(kSlots * SLOT <= 2 * C::STAGE, "four slots fit the LDS tile buffer");
+};
+
+// 2 x 2 waves of 128 x 128 run the four-wave engine.
+template <class C>
+struct UseQuad {
+    static constexpr bool value = C::WM == 2 && C::WN == 2 && C::FM == 4 && C::FN == 4;
+};
+
+// Per-lane LDS offsets, within an operand's slot part, of the fragments of
+// the wave's four 32-wide blocks for the two 16-deep steps of a slot.
+//   TR = false: reduction-contiguous rows of 32 elements (slot_off layout);
+//               a fragment is one 16-byte read.
+//   TR = true:  32 reduction rows of COLS elements (tr_off layout); a
+//               fragment is two transpose reads, rows r and r + 4 (tr_frag).
+template <bool TR, int COLS>
+struct OpFrag {
+    uint32_t off[2][4];
+
+    // first: the wave's first row (TR = false) or column (TR = true).
+    __device__ __forceinline__ void init(int first)
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (TR) {
+                    const int q = lane & 15;
+                    const int row = kk * 16 + 8 * (lane >> 5) + (q >> 2);
+                    const int col = first + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
+                    off[kk][i] = (uint32_t)(tr_off<COLS>(row, col >> 3) + (col & 7) * 2);
+                } else {
+                    off[kk][i] = (uint32_t)slot_off(first + i * 32 + (lane & 31),
+                                                    kk * 2 + (lane >> 5));
+                }
+            }
+    }
+
+    __device__ __forceinline__ bf16x8_t read(const char *part, int kk, int i) const
+    {
+        if constexpr (TR) {
+            typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+            const v4i16_t lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(part + off[kk][i]));
+            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16 *)(part + off[kk][i] + 4 * COLS * 2));
+            const v4i16_t both[2] = {lo, hi};
+            return __builtin_bit_cast(bf16x8_t, both);
+        } else {
+            return *reinterpret_cast<const bf16x8_t *>(part + off[kk][i]);
+        }
+    }
+};
+
+// Fragment registers of the two 16-deep steps of a slot.
+struct QuadFrags {
+    bf16x8_t a0[4], b0[4], a1[4], b1[4];
+};
+
+// Fragment read r (0-3: A blocks, 4-7: B blocks) of step kk of slot q.
+template <class C, bool PART, class FA, class FB>
+__device__ __forceinline__ void quad_read(const char *smem, int q, int kk, int r,
+                                          bf16x8_t (&ta)[4], bf16x8_t (&tb)[4], int ib,
+                                          const FA &fa, const FB &fb)
+{
+    using Q = Quad<C>;
+    const char *base = smem + (q % kSlots) * Q::SLOT;
+    if (r < 4) {
+        if (!PART || r < ib)
+            ta[r] = fa.read(base, kk, r);
+    } else {
+        tb[r - 4] = fb.read(base + Q::A, kk, r - 4);
+    }
+}
+
+// MFMA t (block t / 4, t % 4) of one 16-deep step.
+template <bool PART>
+__device__ __forceinline__ void quad_mma(int t, const bf16x8_t (&ta)[4], const bf16x8_t (&tb)[4],
+                                         f32x16_t (&acc)[4][4], int ib)
+{
+    const int i = t / 4, j = t % 4;
+    if (!PART || i < ib)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i], tb[j], acc[i][j], 0, 0, 0);
+}
+
+// One slot q.  Each phase pairs MFMA t with fragment read t (t < 8) or,
+// at odd t >= 9, with a copy: phase A issues copies 0 .. NCOPY/2 - 1 of
+// slot q + 3, phase B the rest.  COPIES: slot q + 3 exists; NEXT: slot q + 1
+// exists (phase B reads its step 0); WAITN: copies allowed in flight at the
+// barrier (those issued after slot q + 1's: slot q + 2's, and the first half
+// of slot q + 3's).
+template <class C, bool PART, bool COPIES, bool NEXT, int WAITN, class Copy, class FA, class FB>
+__device__ __forceinline__ void quad_slot(const char *smem, int q, f32x16_t (&acc)[4][4],
+                                          QuadFrags &f, Copy &copy, int ib, const FA &fa,
+                                          const FB &fb)
+{
+    using Q = Quad<C>;
+    constexpr int HALF = Q::NCOPY / 2;
+    const int cq = q + kSlots - 1, cbuf = cq % kSlots;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        quad_mma<PART>(t, f.a0, f.b0, acc, ib);
+        if (t < 8)
+            quad_read<C, PART>(smem, q, 1, t, f.a1, f.b1, ib, fa, fb);
+        else if (COPIES && (t & 1) && (t - 9) / 2 < HALF)
+            copy(cq, cbuf, (t - 9) / 2);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_lds();
+    wait_vmcnt<WAITN>();
+    __builtin_amdgcn_sched_barrier(0);
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        quad_mma<PART>(t, f.a1, f.b1, acc, ib);
+        if (t < 8) {
+            if (NEXT)
+                quad_read<C, PART>(smem, q + 1, 0, t, f.a0, f.b0, ib, fa, fb);
+        } else if (COPIES && (t & 1) && (t - 9) / 2 < Q::NCOPY - HALF) {
+            copy(cq, cbuf, HALF + (t - 9) / 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// copy(q, buf, n): this wave's copy n (0 .. NCOPY-1) of reduction slot q into
+// slot buffer buf.
+template <class C, bool PART, class Copy, class FA, class FB>
+__device__ __forceinline__ void quad_body(const char *smem, int nslots, f32x16_t (&acc)[4][4],
+                                          Copy &copy, int ib, const FA &fa, const FB &fb)
+{
+    using Q = Quad<C>;
+    constexpr int N = Q::NCOPY;
+    static_assert(N % 2 == 0 && N / 2 <= 4, "copies fit the odd steps 9..15 of each phase");
+    // Let the compiler see that none of its own memory operations is pending:
+    // otherwise a load still in flight at loop entry (e.g. a register
+    // reload) makes it wait for vmcnt(0) inside the loop, which would also
+    // drain the copies it does not know about.
+    __builtin_amdgcn_s_waitcnt(0);
+    QuadFrags f;
+    const int pre = min(kSlots - 1, nslots);
+    for (int q = 0; q < pre; ++q)
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            copy(q, q, n);
+    wait_batch<N>(pre - 1);
+    wg_barrier();
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        quad_read<C, PART>(smem, 0, 0, r, f.a0, f.b0, ib, fa, fb);
+    int q = 0;
+    for (; q + kSlots - 1 < nslots; ++q)
+        quad_slot<C, PART, true, true, N + N / 2>(smem, q, acc, f, copy, ib, fa, fb);
+    // The last (up to) three slots: no more copies.
+    if (q + 2 < nslots)
+        quad_slot<C, PART, false, true, N>(smem, q++, acc, f, copy, ib, fa, fb);
+    if (q + 1 < nslots)
+        quad_slot<C, PART, false, true, 0>(smem, q++, acc, f, copy, ib, fa, fb);
+    quad_slot<C, PART, false, false, 0>(smem, q, acc, f, copy, ib, fa, fb);
+}
+
+// A_TR / B_TR: operand layout (OpFrag).  rows: real rows of the tile (A
+// side); waves of a ragged tail skip the MFMAs and A reads of their padding
+// 32-row blocks but keep every barrier.  Leaves LDS free for the epilogue
+// (all reads and copies complete).
+template <class C, bool A_TR, bool B_TR, class Copy>
+__device__ __forceinline__ void mainloop_quad(const char *smem, int nslots,
+                                              f32x16_t (&acc)[C::FM][C::FN], Copy copy, int rows)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    if (nslots <= 0)
+        return;
+    OpFrag<A_TR, C::BM> fa;
+    OpFrag<B_TR, C::BN> fb;
+    fa.init(wm * C::TM);
+    fb.init(wn * C::TN);
+    const int ib = __builtin_amdgcn_readfirstlane(
+        min(C::FM, max(0, (rows - wm * C::TM + 31) / 32)));
+    if (ib == C::FM)
+        quad_body<C, false>(smem, nslots, acc, copy, ib, fa, fb);
+    else
+        quad_body<C, true>(smem, nslots, acc, copy, ib, fa, fb);
+}
+
+// A row-major slot tile (32 reduction rows of COLS elements), copied by the
+// four waves: 1 KiB windows of RW = 64 / (COLS / 8) rows, NC per wave.  Lane
+// l writes window row l / CPR at physical chunk l % CPR and fetches the
+// logical chunk that tr_off maps there.  The HBM rows of the reduction
+// indices are contiguous (red -> first_row + red) with pitch row_bytes.
+template <int COLS, int NC>
+struct SlotTileCopier {
+    static constexpr int CPR = COLS / 8, RW = kWave / CPR;
+    static_assert(4 * NC * RW == SK, "four waves cover the slot's rows");
+    uint32_t off[NC];  // HBM byte offset of (row, chunk) at slot 0 (kOOB: column outside)
+    int row[NC];       // slot row of this lane in window j
+    uint32_t lds0;     // LDS address of the wave's first window in slot 0
+    int64_t row_bytes;
+
+    __device__ __forceinline__ void init(char *slot0_part, int first_row, int col0, int ncols,
+                                         int64_t row_bytes_)
+    {
+        const int lane = threadIdx.x & (kWave - 1);
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        row_bytes = row_bytes_;
+        lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(
+                   (__attribute__((address_space(3))) char *)slot0_part)) +
+               wave * NC * kWave * 16;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int r = (wave * NC + j) * RW + lane / CPR;
+            const int lc = (lane % CPR) ^ ((r & 3) << 2);
+            const int col = col0 + lc * 8;
+            row[j] = r;
+            off[j] = col < ncols ? (uint32_t)((first_row + r) * row_bytes) + (uint32_t)col * 2
+                                 : kOOB;
+        }
+    }
+    // Copy j of reduction slot q into slot buffer `slot`; rows at or past
+    // nred are zeros.
+    template <int SLOT_BYTES>
+    __device__ __forceinline__ void issue_one(const u32x4_t &r, int j, int slot, int q,
+                                              int nred) const
+    {
+        const bool in = q * SK + row[j] < nred;
+        copy16_to_lds(r, in ? off[j] : kOOB,
+                      __builtin_amdgcn_readfirstlane((uint32_t)(q * SK * row_bytes)),
+                      lds0 + (uint32_t)(slot * SLOT_BYTES + j * kWave * 16));
+    }
+};
+
 // Row and column of accumulator element r of 32x32 block (i, j) for this lane.
 template <class C>
 __device__ __forceinline__ int acc_row(int wm, int i, int r)
@@ -559,7 +939,7 @@ __device__ __forceinline__ int acc_col(int wn, int j)
 // st1), then copied out as 16-byte row segments.  Each lane addresses its
 // accumulators from one base pointer plus compile-time offsets.
 // s_dst[i]: destination row of tile row i (-1: skip); s_scale: per-row factor
-// applied when `scale` is set.  Y is bf16 with leading dimension ldy; tile
+// applied when SCALE is set.  Y is bf16 with leading dimension ldy; tile
 // column c maps to output column n0 + c (valid below ncols).
 template <class C>
 struct EpiLayout {
@@ -569,6 +949,7 @@ struct EpiLayout {
     static_assert(ROWS_PER_BUF % C::TM == 0, "a wave's rows must stay in one staging buffer");
 };
 
+// SCALE: multiply row i by s_scale[i].
 template <class C, bool SCALE>
 __device__ __forceinline__ void stage_bf16(char *st0, char *st1,
                                            const f32x16_t (&acc)[C::FM][C::FN],
@@ -583,6 +964,9 @@ __device__ __forceinline__ void stage_bf16(char *st0, char *st1,
     uint16_t *base = reinterpret_cast<uint16_t *>(buf) +
                      (row0 % L::ROWS_PER_BUF) * C::BN + wn * C::TN + (lane & 31);
     const float *sc = s_scale + row0;
+    // Straight-line code, one output row of the wave's blocks at a time
+    // (sched_barrier): otherwise the compiler moves every accumulator out of
+    // the AGPRs, and loads every row factor, up front.
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -592,20 +976,18 @@ __device__ __forceinline__ void stage_bf16(char *st0, char *st1,
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
                 base[rr * C::BN + j * 32] = to_bf16(SCALE ? acc[i][j][r] * f : acc[i][j][r]);
+            __builtin_amdgcn_sched_barrier(0);
         }
 }
 
-template <class C>
+template <class C, bool SCALE = false>
 __device__ __forceinline__ void epilogue_bf16(char *st0, char *st1,
                                               const f32x16_t (&acc)[C::FM][C::FN],
-                                              const int *s_dst, const float *s_scale, bool scale,
+                                              const int *s_dst, const float *s_scale,
                                               char *Y, int64_t ldy, int n0, int ncols)
 {
     using L = EpiLayout<C>;
-    if (scale)
-        stage_bf16<C, true>(st0, st1, acc, s_scale);
-    else
-        stage_bf16<C, false>(st0, st1, acc, s_scale);
+    stage_bf16<C, SCALE>(st0, st1, acc, s_scale);
     __syncthreads();
     constexpr int CPR = C::BN / 8;  // 16-byte chunks per tile row
     for (int idx = threadIdx.x; idx < C::BM * CPR; idx += C::NT) {
@@ -697,8 +1079,8 @@ __device__ __forceinline__ int checked_gather(const int32_t *gather, int64_t p, 
 template <class C>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 {
-    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
-    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    char *const st0 = smem, *const st1 = smem + C::STAGE;
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_src[C::BM];
@@ -746,6 +1128,10 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
         }
         __syncthreads();
 
+        const u32x4_t wr =
+            rsrc_words(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
+        f32x16_t acc[C::FM][C::FN];
+        zero_acc<C>(acc);
         RowLoader<C::BM, C::NT, MOEGG_FWD_DMA != 0> la;
         RowLoader<C::BN, C::NT, MOEGG_FWD_DMA != 0> lb;
 #pragma unroll
@@ -756,11 +1142,6 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             const int r = lb.tile_row(i);
             lb.set_row(i, n0 + r < a.N ? n0 + r : -1, row_bytes);
         }
-        const u32x4_t wr =
-            rsrc_words(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
-
-        f32x16_t acc[C::FM][C::FN];
-        zero_acc<C>(acc);
         mainloop<C, true, false, false>(
             st0, st1, nsteps, acc,
             [&](int s, char *As, char *Bs) {
@@ -772,7 +1153,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
                 lb.store(Bs);
             },
             rows);
-        epilogue_bf16<C>(st0, st1, acc, s_dst, s_scale, fm, a.Y, a.N, n0, a.N);
+        epilogue_bf16<C, true>(st0, st1, acc, s_dst, s_scale, a.Y, a.N, n0, a.N);
     }
 }
 
@@ -783,8 +1164,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 template <class C>
 __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 {
-    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
-    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    char *const st0 = smem, *const st1 = smem + C::STAGE;
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_src[C::BM];
@@ -825,14 +1206,40 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         }
         __syncthreads();
 
+        const u32x4_t wr =
+            rsrc_words(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
+        f32x16_t acc[C::FM][C::FN];
+        if constexpr (UseQuad<C>::value) {
+            // Wave w copies dY rows [64 w, 64 w + 64) (A, reduction-contiguous)
+            // and W rows 8 w .. 8 w + 7 of each slot (B, row-major).
+            using Q = Quad<C>;
+            const int first = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * 64;
+            SlotCopier<Q::NCA> ca;
+            SlotTileCopier<C::BN, Q::NCB> cb;
+            ca.init(smem, first);
+#pragma unroll
+            for (int j = 0; j < Q::NCA; ++j)
+                ca.set_row(j, s_src[ca.row(first, j)], dy_row);
+            cb.init(smem + Q::A, 0, k0, a.K, w_row);
+            const int N = a.N;
+            zero_acc<C>(acc);
+            mainloop_quad<C, false, true>(
+                smem, (N + SK - 1) / SK, acc,
+                [&](int q, int buf, int n) {
+                    if (n < Q::NCA)
+                        ca.template issue_one<Q::SLOT>(dyr, n, buf, q * SK, N);
+                    else
+                        cb.template issue_one<Q::SLOT>(wr, n - Q::NCA, buf, q, N);
+                },
+                rows);
+            epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+            continue;
+        }
         RowLoader<C::BM, C::NT, MOEGG_DX_DMA != 0> la;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], dy_row);
-        const u32x4_t wr =
-            rsrc_words(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
         const int N = a.N;
-        f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         if constexpr (MOEGG_TILE_DMA != 0) {
             TileDmaLoader<C::BN, C::NT> lb;
@@ -868,7 +1275,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                 },
             rows);
         }
-        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, a.dX, a.K, k0, a.K);
+        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
     }
 }
 
@@ -1036,7 +1443,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         if (f32out)
             epilogue_f32<C>(acc, s_dst, reinterpret_cast<float *>(a.dW), a.K, k0, a.K);
         else
-            epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, a.dW, a.K, k0, a.K);
+            epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dW, a.K, k0, a.K);
     }
 }
 
@@ -1125,8 +1532,7 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
             },
             min(C::BM, g.m - m0));
         }
-        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, false, static_cast<char *>(g.y), g.ldy, n0,
-                         g.n);
+        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, static_cast<char *>(g.y), g.ldy, n0, g.n);
     }
 }
 
@@ -1149,6 +1555,7 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
 #endif
 using BigCfg = Cfg<MOEGG_FWD_CFG>;       // many rows per expert
 using DxCfg = Cfg<MOEGG_DX_CFG>;
+using DxQuadCfg = Cfg<256, 256, 2, 2>;  // long reductions: four-wave engine
 using DwCfg = Cfg<MOEGG_DW_CFG>;
 using SmallCfg = Cfg<MOEGG_SMALL_CFG>;   // few rows per expert: stream the weights
 using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
@@ -1157,6 +1564,7 @@ using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
 template __global__ void fwd_kernel<BigCfg>(FwdParams);
 template __global__ void fwd_kernel<SmallCfg>(FwdParams);
 template __global__ void dx_kernel<DxCfg>(DxParams);
+template __global__ void dx_kernel<DxQuadCfg>(DxParams);
 template __global__ void dw_kernel<DwCfg, false, false>(DwParams);
 template __global__ void dw_kernel<DwCfg, true, false>(DwParams);
 template __global__ void dw_kernel<DwCfg, false, true>(DwParams);
@@ -1204,12 +1612,25 @@ hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
+template <class C>
+static void dx_launch_cfg(const DxParams &p, int cus, hipStream_t stream)
 {
-    using C = DxCfg;
     const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.K + C::BN - 1) / C::BN);
     static int res = resident_blocks(dx_kernel<C>, C::NT);
     hipLaunchKernelGGL(dx_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+}
+
+// Measured on MI355X: the four-wave engine is faster once the reduction (N)
+// is long enough to amortise its per-tile prologue (T=4096 top-2, N=28672:
+// 2.16 ms against 2.44 ms); at N = 2048 the eight-wave engine is.
+constexpr int kDxQuadMinN = 8192;
+
+hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
+{
+    if (p.N >= kDxQuadMinN)
+        dx_launch_cfg<DxQuadCfg>(p, cus, stream);
+    else
+        dx_launch_cfg<DxCfg>(p, cus, stream);
     return hipGetLastError();
 }
 

@@ -71,6 +71,10 @@ def _load():
         lib.oracle_grouped_gemm_dW.restype = None
         lib.oracle_dense_gemm_kn.argtypes = [vp, vp, i32, i32, i32, vp]
         lib.oracle_dense_gemm_kn.restype = None
+        lib.oracle_combine.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        lib.oracle_combine.restype = None
+        lib.oracle_combine_bwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, vp]
+        lib.oracle_combine_bwd.restype = None
         _lib = lib
     return _lib
 
@@ -199,3 +203,34 @@ def dense_gemm_kn(X, W):
     Y = np.zeros((m, n), np.float32)
     _load().oracle_dense_gemm_kn(_ptr(X), _ptr(W), m, n, k, _ptr(Y))
     return Y
+
+
+def combine(Y, topk: int, scatter=None, weights=None, num_tokens=None):
+    """Top-k combine: out[t] = sum_j w[t*k+j] * Y[row(t*k+j)] (fp32).
+
+    Y: uint16 [rows, N]; scatter: int32 [T*k] (Y in expert-sorted order) or
+    None (Y in slot order, rows = T*k); weights: float32 [T*k] or None (1).
+    Returns float32 [T, N].
+    """
+    Y = _bf16_bits(Y)
+    N = int(Y.shape[1])
+    scatter = _c(scatter, np.int32)
+    weights = _c(weights, np.float32)
+    S = int(scatter.size) if scatter is not None else int(Y.shape[0])
+    T = S // topk if num_tokens is None else int(num_tokens)
+    out = np.zeros((T, N), np.float32)
+    _load().oracle_combine(_ptr(Y), _ptr(scatter), _ptr(weights), T, topk, N, _ptr(out))
+    return out
+
+
+def combine_bwd(dOut, Y, topk: int, scatter=None, weights=None):
+    """Backward of combine: (dY float32 [rows of Y, N] (unmapped rows 0), dw float32 [T*k])."""
+    dOut, Y = _bf16_bits(dOut), _bf16_bits(Y)
+    T, N = dOut.shape
+    scatter = _c(scatter, np.int32)
+    weights = _c(weights, np.float32)
+    dY = np.zeros(Y.shape, np.float32)
+    dw = np.zeros(T * topk, np.float32)
+    _load().oracle_combine_bwd(_ptr(dOut), _ptr(Y), _ptr(scatter), _ptr(weights), T, topk, N,
+                               _ptr(dY), _ptr(dw))
+    return dY, dw

@@ -294,3 +294,64 @@ void oracle_dense_gemm_kn(const uint16_t *X, const uint16_t *W, int32_t m, int32
             Y[(int64_t)i * n + j] = acc;
         }
 }
+
+/*
+ * Top-k combine: the unpermute of the pages (unpermute in
+ * wall_x/fusions/backend.py: expert outputs back to token order, the top-k
+ * copies of a token weighted by their routing probabilities and summed),
+ * which is also the n_expts_act reduction at the end of matmul_ogs_torch
+ * (triton_kernels/matmul_ogs.py):
+ *   out[t, n] = sum_{j < k} w[t*k + j] * Y[row(t*k + j), n]   (fp32, j ascending)
+ *   row(s) = scatter[s] when Y is in expert-sorted order (scatter != NULL;
+ *            a negative entry is a dropped slot and adds nothing), else s
+ *            (Y already in slot order, the permute_y output);
+ *   w = 1 when NULL (matmul_ogs's form, whose rows already carry the gates).
+ * out is [T, N] fp32.
+ */
+void oracle_combine(const uint16_t *Y, const int32_t *scatter, const float *w, int64_t T,
+                    int32_t topk, int32_t N, float *out)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int32_t j = 0; j < topk; ++j) {
+                int64_t s = t * topk + j;
+                int64_t row = scatter ? scatter[s] : s;
+                if (row < 0)
+                    continue;
+                float ws = w ? w[s] : 1.0f;
+                acc += ws * widen_bf16(Y[row * N + n]);
+            }
+            out[t * N + n] = acc;
+        }
+}
+
+/*
+ * Backward of the combine (unpermute_bwd, wall_x/fusions/backend.py, which
+ * takes the forward's input so that the probabilities get a gradient too):
+ *   dY[row(s), n] = w[s] * dOut[t, n]                     (fp32)
+ *   dw[s]         = sum_n dOut[t, n] * Y[row(s), n]       (fp32, n ascending)
+ * for s = t*k + j, with row() and w as in oracle_combine.  A dropped slot
+ * (row < 0) writes no dY row and has dw = 0.  dY is [rows of Y, N] fp32 and
+ * only the rows some slot maps to are written; dw is [T*k] (may be NULL).
+ */
+void oracle_combine_bwd(const uint16_t *dOut, const uint16_t *Y, const int32_t *scatter,
+                        const float *w, int64_t T, int32_t topk, int32_t N, float *dY, float *dw)
+{
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < topk; ++j) {
+            int64_t s = t * topk + j;
+            int64_t row = scatter ? scatter[s] : s;
+            float ws = w ? w[s] : 1.0f;
+            float acc = 0.0f;
+            if (row >= 0) {
+                for (int32_t n = 0; n < N; ++n) {
+                    float g = widen_bf16(dOut[t * N + n]);
+                    dY[row * N + n] = ws * g;
+                    acc += g * widen_bf16(Y[row * N + n]);
+                }
+            }
+            if (dw)
+                dw[s] = acc;
+        }
+}

@@ -129,6 +129,44 @@ def build_dual_step(wl):
     return st
 
 
+def build_combine_step(wl, rotate=2):
+    """Top-k combine after the fine-grained down projection (expert-sorted Y,
+    scatter index and routing weights) and its backward with the weight
+    gradient.  Y is rotated over `rotate` copies so that the 256 MB MALL does
+    not hold it between steps."""
+    st = Step("combine")
+    S, T, N, k = wl.S, wl.T, wl.N, wl.topk
+    ids = _dev(wl.ids)
+    route_out = mg.moe_route(ids, wl.E, BLOCK_M)
+    g = synth.generator(synth.SEEDS["combine_y"])
+    Ys = [_dev(synth.normal_bf16((S, N), 1.0, g))]
+    for _ in range(1, rotate):
+        Ys.append(Ys[0].clone())
+    dOut = _dev(synth.normal_bf16((T, N), 0.1, g))
+    w = _dev(wl.weights.reshape(-1).contiguous())
+    out = torch.empty(T, N, dtype=torch.bfloat16, device="cuda")
+    dY = torch.empty(S, N, dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(S, dtype=torch.float32, device="cuda")
+    it = {"f": 0, "b": 0}
+
+    def fwd():
+        Y = Ys[it["f"] % len(Ys)]
+        it["f"] += 1
+        mg.combine(Y, k, route_out["scatter"], w, out=out)
+
+    def bwd():
+        Y = Ys[it["b"] % len(Ys)]
+        it["b"] += 1
+        mg.combine_bwd(dOut, Y, k, route_out["scatter"], w, dY=dY, dw=dw)
+
+    # useful FLOPs: one multiply-add per slot element (fwd); two per element (bwd)
+    st.add("combine", fwd, 2.0 * S * N, S * N * 2 + S * 8 + T * N * 2)
+    st.add("combine_bwd", bwd, 4.0 * S * N, T * N * 2 + S * N * 2 + S * 8 + S * N * 2 + S * 4)
+    st.m_sizes = route_out["m_sizes"].cpu().numpy()
+    st.inputs = wl
+    return st
+
+
 def make_step(name):
     if name == "mixtral":
         return build_layer_step(synth.mixtral(), dY_seed=synth.SEEDS["mixtral_bwd_dy"])
@@ -142,6 +180,8 @@ def make_step(name):
         return build_layer_step(synth.tiny(), dY_seed=0, with_bwd=False)
     if name == "dual":
         return build_dual_step(synth.dual())
+    if name == "combine":
+        return build_combine_step(synth.fine_down())
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -154,6 +194,8 @@ WORKLOAD_DESC = {
     "decode": "fine-grained MoE down grouped GEMM decode slice, T=64 E=128 top-8 K=768 N=2048",
     "dual": "asymmetric dual-expert GEMM: [512,1024]x[1024,2048] and [256,1024]x[1024,4096]",
     "tiny": "tiny MoE grouped GEMM, T=128 K=256 N=512 E=8 top-2, permute_x",
+    "combine": "top-k combine after the fine-grained down projection, T=8192 top-8 N=2048 "
+               "(expert-sorted Y, routing weights) and its backward with the weight gradient",
 }
 
 
@@ -213,6 +255,22 @@ def cpu_baseline(st, budget_s):
     import oracle
 
     wl = st.inputs
+    if st.name == "combine":
+        # the whole forward combine of the workload, repeated up to ~budget_s
+        g = synth.generator(synth.SEEDS["combine_y"])
+        Yb = synth.bits(synth.normal_bf16((wl.S, wl.N), 1.0, g))
+        ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, BLOCK_M)
+        w = wl.weights.numpy().reshape(-1)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.combine(Yb, wl.topk, scatter=ref_route["scatter"], weights=w)
+            reps += 1
+            if time.perf_counter() - t0 >= min(budget_s, 10.0) or reps >= 50:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": 2.0 * wl.S * wl.N * reps / dt / 1e12, "unit": "TFLOP/s", "cores": 1,
+                "kind": "oracle", "sample": f"{reps} full forward combine(s) of T={wl.T} "
+                f"top-{wl.topk} N={wl.N}", "seconds": round(dt, 3)}
     if st.name == "dual":
         x, w = wl.groups[0]
         per_row = 2.0 * x.shape[1] * w.shape[1]
@@ -265,7 +323,8 @@ def copy_calibration(nbytes=1 << 30, reps=5):
     return 0
 
 
-KERNEL_LABELS = (("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
+KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
+                 ("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),
                  ("route_scan", "route_scan"), ("route_scatter", "route_scatter"))
 
@@ -326,7 +385,7 @@ def summarize(prof_dir, workload, command):
               "1 GiB device copy read by the same counters):".format(cal["FETCH_SIZE"],
                                                                   cal["WRITE_SIZE"]), "",
               "| kernel | read MB | written MB |", "|---|---|---|"]
-    for lab in ("fwd", "dX", "dW", "groups"):
+    for lab in ("fwd", "dX", "dW", "groups", "combine", "combine_bwd"):
         if lab in fetch and lab in write:
             rd = fetch[lab] * 1024 * cal["FETCH_SIZE"]
             wr = write[lab] * 1024 * cal["WRITE_SIZE"]

@@ -82,11 +82,12 @@ size_t moegg_route_workspace_bytes(int64_t num_slots, int32_t num_experts);
 /*
  * moegg_route -- expert histogram, offsets and stable gather/scatter indices.
  *
- * Follows the routing metadata the pages consume: m_sizes ("tokens assigned
- * to each expert", grouped_gemm_forward docstring, grouped_gemm/interface.py),
- * expt_hist and its cumsum offsets, the block-padded layout of the ragged dw
- * comment block, and GatherIndx / ScatterIndx ("dst_idx[src_idx] = arange")
- * in triton_kernels/matmul_ogs.py.
+ * Follows the routing metadata the pages consume: m_sizes (the per-expert
+ * slot counts of the grouped_gemm_forward docstring,
+ * grouped_gemm/interface.py), expt_hist and its cumsum offsets, the
+ * block-padded layout of the ragged dw comment block, and GatherIndx /
+ * ScatterIndx in triton_kernels/matmul_ogs.py, where the scatter index is
+ * the inverse permutation of the gather index.
  *
  *   topk_ids       [S] int32, slot order (the router's [T, k] ids).
  *   m_sizes        out [E]   number of slots routed to each expert.
@@ -169,8 +170,9 @@ moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t 
  * moegg_grouped_gemm_dW -- dW_e = dY_e^T X_e, a reduction over each expert's
  * own (ragged) number of rows, one launch.
  *
- * grouped_gemm_dW (grouped_gemm/interface.py) and the ragged-K
- * "dw = matmul_ogs(x.T, dy)" formulation of triton_kernels/matmul_ogs.py:
+ * grouped_gemm_dW (grouped_gemm/interface.py) and the ragged-K formulation of
+ * triton_kernels/matmul_ogs.py, which computes dw as a grouped matmul of x
+ * transposed with dy:
  *   dW[e, n, k] = sum_{p in e} dY[q(p), n] * X[r(p), k]  (fp32 accumulation)
  *   r(p) = gather_idx[p] / topk with PERMUTE_X (X is [T, K]), else p
  *   (X is [S, K]); q(p) = gather_idx[p] with PERMUTE_Y, else p.
@@ -200,8 +202,8 @@ typedef struct {
 /*
  * moegg_grouped_gemm_groups -- several independent GEMMs of different shapes
  * in one launch: the asymmetric dual-expert GEMM of asym_dual_gmm_separated
- * ("output_expert0 = input_expert0 @ weight_expert0, output_expert1 =
- * input_expert1 @ weight_expert1 ... as a single fused kernel call").
+ * (wall_x/fusions/backend.py), which multiplies each expert's own input by
+ * its own weight and computes both products in one fused call.
  *
  *   groups      HOST array of num_groups descriptors (copied at launch; it
  *               may be freed when the call returns).  1 <= num_groups <=
@@ -214,6 +216,63 @@ typedef struct {
  */
 moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_groups,
                                        int32_t trans_b, void *stream);
+
+/* Combine flag: write the combine's output in fp32 instead of bf16. */
+#define MOEGG_COMBINE_FP32_OUT 16u
+
+/*
+ * moegg_combine -- the top-k combine after the second grouped GEMM: each
+ * token's k expert outputs, weighted by their routing probabilities and
+ * summed.  This is the unpermute of wall_x/fusions/backend.py (expert outputs
+ * back to token order, combined with the routing probabilities) and the
+ * n_expts_act reduction at the end of matmul_ogs in
+ * triton_kernels/matmul_ogs.py (matmul_ogs_torch accumulates it in fp32):
+ *
+ *   out[t, n] = sum_{j<k} w[t*k + j] * Y[row(t*k + j), n]   (fp32, j ascending)
+ *
+ *   Y              [y_rows, N] bf16 device, row-major.
+ *   scatter_idx    [T*k] int32 device: row of Y holding slot s (moegg_route's
+ *                  scatter_idx when Y is in expert-sorted order); a negative
+ *                  entry is a dropped slot and adds nothing.  NULL: Y is in
+ *                  slot order (the PERMUTE_Y output), row(s) = s, and
+ *                  y_rows >= T*k.
+ *   topk_weights   [T*k] fp32 device, slot order, or NULL for weight 1 (the
+ *                  rows already carry the gates, as after FUSE_MUL_POST).
+ *   flags          0 or MOEGG_COMBINE_FP32_OUT.
+ *   out            [T, N] device, bf16 (rounded once from the fp32 sum) or
+ *                  fp32.  Every element is written.
+ *   error_flags    optional device int32; an entry of scatter_idx at or above
+ *                  y_rows sets MOEGG_DERR_GATHER and the slot is skipped.
+ * N must be a multiple of 8; Y and out 16-byte aligned.  T = 0 is a no-op.
+ * Errors: ESHAPE for bad sizes, EINVAL for unknown flags, NULL or misaligned
+ * pointers.
+ */
+moegg_status moegg_combine(const void *Y, const int32_t *scatter_idx, const float *topk_weights,
+                           int64_t num_tokens, int32_t topk, int32_t N, int64_t y_rows,
+                           uint32_t flags, void *out, int32_t *error_flags, void *stream);
+
+/*
+ * moegg_combine_bwd -- backward of moegg_combine (unpermute_bwd,
+ * wall_x/fusions/backend.py, which takes the forward input so that the
+ * routing probabilities get a gradient as well):
+ *
+ *   dY[row(s), n] = w[s] * dOut[t, n]                    (rounded to bf16)
+ *   dw[s]         = sum_n dOut[t, n] * Y[row(s), n]      (fp32)
+ *
+ * for s = t*k + j, with row() and w as in moegg_combine (w = 1 when
+ * topk_weights is NULL).
+ *   dOut   [T, N] bf16 device.
+ *   Y      the forward's input [y_rows, N] bf16; read only when dw != NULL.
+ *   dY     [y_rows, N] bf16 device; only rows some slot maps to are written
+ *          (all of them when scatter_idx is a permutation or NULL).
+ *   dw     [T*k] fp32 device, or NULL to skip the weight gradient.  A dropped
+ *          slot gets dw = 0 and writes no dY row.
+ * Alignment, sizes and errors as moegg_combine.
+ */
+moegg_status moegg_combine_bwd(const void *dOut, const void *Y, const int32_t *scatter_idx,
+                               const float *topk_weights, int64_t num_tokens, int32_t topk,
+                               int32_t N, int64_t y_rows, void *dY, float *dw,
+                               int32_t *error_flags, void *stream);
 
 #ifdef __cplusplus
 }

@@ -70,13 +70,13 @@ int64_t oracle_n_blocks(int64_t n_rows, int32_t n_experts, int32_t block_m)
  *            tile of each expert.
  * gather[p]: slot id held at sorted position p.  Positions are assigned by
  *            walking slots in ascending order and handing each one the next
- *            free position of its expert (a stable counting sort), so
- *            "slicing gather_indices by cumsum of m_sizes gives the indices
- *            of tokens assigned to each expert" (grouped_gemm_forward
- *            docstring) with slots in ascending order inside each expert.
- * scatter[s]: the inverse, sorted position of slot s
- *            (dst_idx[src_idx] = arange, GatherIndx/ScatterIndx in
- *            triton_kernels/matmul_ogs.py); -1 marks a slot whose id is
+ *            free position of its expert (a stable counting sort).  Cutting
+ *            gather at the cumulative m_sizes then yields each expert's slots
+ *            (the grouped_gemm_forward docstring relies on this), here in
+ *            ascending slot order inside each expert.
+ * scatter[s]: the inverse, sorted position of slot s (the inverse
+ *            permutation that GatherIndx/ScatterIndx in
+ *            triton_kernels/matmul_ogs.py describe); -1 marks a slot whose id is
  *            outside [0, E) and was therefore dropped.  gather[p] = -1 for
  *            the positions such dropped slots leave unused at the end.
  *
@@ -238,8 +238,8 @@ void oracle_grouped_gemm_dX(const uint16_t *dY, const uint16_t *W, const int32_t
 /*
  * dW of the grouped GEMM -- grouped_gemm_dW (grouped_gemm/interface.py):
  * dW_e = dY_e^T * X_e, a reduction over the m_sizes[e] rows of expert e
- * (a ragged reduction length, the "dw = matmul_ogs(x.T, dy)" formulation of
- * triton_kernels/matmul_ogs.py):
+ * (a ragged reduction length; triton_kernels/matmul_ogs.py computes dw the
+ * same way, as a grouped matmul of x transposed with dy):
  *   dW[e, n, k] = sum_{p in e} dY[q(p), n] * X[r(p), k]   (fp32, p ascending)
  *   r(p) = gather[p] / topk with permute_x, else p;
  *   q(p) = gather[p] with permute_y, else p.

@@ -42,7 +42,7 @@ FUSE_MUL_POST = 4
 
 # Seeds: 1000 + the workload's number; the decode slice and dY have their own.
 SEEDS = {"tiny": 1001, "dual": 1002, "mixtral": 1003, "fine_down": 1004,
-         "fine_bwd_dy": 1005, "fine_decode": 1041, "mixtral_bwd_dy": 2003}
+         "fine_bwd_dy": 1005, "fine_decode": 1041, "mixtral_bwd_dy": 2003, "combine_y": 1046}
 
 
 def generator(seed: int) -> torch.Generator:

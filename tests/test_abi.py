@@ -121,3 +121,24 @@ def test_groups_checks(lib):
     assert lib.moegg_grouped_gemm_groups(g, 17, 0, None) == ESHAPE
     g[1] = mg.MoeggGroup(1 << 20, 1 << 20, 1 << 20, 16, 64, 64, 32, 64, 64)  # ldx < k
     assert lib.moegg_grouped_gemm_groups(g, 2, 0, None) == ESHAPE
+
+
+def test_combine_checks(lib):
+    CF32 = 16
+    # N not a multiple of 8; negative tokens; slot-order Y with too few rows
+    assert lib.moegg_combine(FAKE, None, None, 10, 2, 60, 20, 0, FAKE, None, None) == ESHAPE
+    assert lib.moegg_combine(FAKE, None, None, -1, 2, 64, 20, 0, FAKE, None, None) == ESHAPE
+    assert lib.moegg_combine(FAKE, None, None, 10, 2, 64, 19, 0, FAKE, None, None) == ESHAPE
+    assert lib.moegg_combine(FAKE, None, None, 10, 0, 64, 20, 0, FAKE, None, None) == ESHAPE
+    # unknown flag, NULL output
+    assert lib.moegg_combine(FAKE, None, None, 10, 2, 64, 20, 32, FAKE, None, None) == EINVAL
+    assert lib.moegg_combine(FAKE, None, None, 10, 2, 64, 20, CF32, None, None, None) == EINVAL
+    # zero tokens: no-op even with NULL pointers
+    assert lib.moegg_combine(None, None, None, 0, 2, 64, 0, 0, None, None, None) == 0
+    # backward: dw needs the forward input
+    assert lib.moegg_combine_bwd(FAKE, None, None, None, 10, 2, 64, 20, FAKE, FAKE, None,
+                                 None) == EINVAL
+    assert lib.moegg_combine_bwd(FAKE, FAKE, None, None, 10, 2, 60, 20, FAKE, None, None,
+                                 None) == ESHAPE
+    assert lib.moegg_combine_bwd(None, None, None, None, 0, 2, 64, 0, None, None, None,
+                                 None) == 0

@@ -77,6 +77,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moegg_grouped_gemm_dW.restype = ctypes.c_int
     lib.moegg_grouped_gemm_groups.argtypes = [ctypes.POINTER(MoeggGroup), i32, i32, vp]
     lib.moegg_grouped_gemm_groups.restype = ctypes.c_int
+    lib.moegg_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, u32, vp, vp, vp]
+    lib.moegg_combine.restype = ctypes.c_int
+    lib.moegg_combine_bwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, i64, vp, vp, vp, vp]
+    lib.moegg_combine_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -230,3 +234,51 @@ def grouped_gemm_groups(groups, trans_b: int = 0, *, outputs=None, stream=None):
     _check(lib.moegg_grouped_gemm_groups(arr, len(groups), int(trans_b), _stream(stream)),
            "moegg_grouped_gemm_groups")
     return ys
+
+
+COMBINE_FP32_OUT = 16
+
+
+def combine(Y, topk: int, scatter_idx=None, topk_weights=None, *, num_tokens=None,
+            fp32_out: bool = False, out=None, error_flags=None, stream=None):
+    """Top-k combine (moegg_combine): out[t] = sum_j w[t*k+j] * Y[row(t*k+j)].
+
+    Y: bf16 [rows, N]; scatter_idx: int32 [T*k] (Y in expert-sorted order) or
+    None (Y in slot order); topk_weights: float32 [T*k] or None (weight 1).
+    Returns out [T, N], bf16 (fp32 with fp32_out).
+    """
+    lib = load_library()
+    Y = _device_tensor(Y, torch.bfloat16, "Y")
+    scatter_idx = _device_tensor(scatter_idx, torch.int32, "scatter_idx")
+    topk_weights = _device_tensor(topk_weights, torch.float32, "topk_weights")
+    S = scatter_idx.numel() if scatter_idx is not None else Y.shape[0]
+    T = S // topk if num_tokens is None else int(num_tokens)
+    N = Y.shape[1]
+    if out is None:
+        out = torch.empty(T, N, dtype=torch.float32 if fp32_out else torch.bfloat16,
+                          device=Y.device)
+    _check(lib.moegg_combine(_ptr(Y), _ptr(scatter_idx), _ptr(topk_weights), T, topk, N,
+                             Y.shape[0], COMBINE_FP32_OUT if fp32_out else 0, _ptr(out),
+                             _ptr(error_flags), _stream(stream)), "moegg_combine")
+    return out
+
+
+def combine_bwd(dOut, Y, topk: int, scatter_idx=None, topk_weights=None, *, want_dw=True,
+                dY=None, dw=None, error_flags=None, stream=None):
+    """Backward of combine (moegg_combine_bwd): returns (dY bf16 [rows, N], dw float32 [T*k]
+    or None).  Y (the forward input) is read only for dw."""
+    lib = load_library()
+    dOut = _device_tensor(dOut, torch.bfloat16, "dOut")
+    Y = _device_tensor(Y, torch.bfloat16, "Y")
+    scatter_idx = _device_tensor(scatter_idx, torch.int32, "scatter_idx")
+    topk_weights = _device_tensor(topk_weights, torch.float32, "topk_weights")
+    T, N = dOut.shape
+    rows = Y.shape[0] if Y is not None else T * topk
+    if dY is None:
+        dY = torch.empty(rows, N, dtype=torch.bfloat16, device=dOut.device)
+    if want_dw and dw is None:
+        dw = torch.empty(T * topk, dtype=torch.float32, device=dOut.device)
+    _check(lib.moegg_combine_bwd(_ptr(dOut), _ptr(Y), _ptr(scatter_idx), _ptr(topk_weights), T,
+                                 topk, N, rows, _ptr(dY), _ptr(dw if want_dw else None),
+                                 _ptr(error_flags), _stream(stream)), "moegg_combine_bwd")
+    return dY, (dw if want_dw else None)

@@ -55,7 +55,7 @@ moegg_status check_permute_flags(uint32_t flags, const int32_t *gather_idx, int6
 {
     const bool px = flags & MOEGG_PERMUTE_X, py = flags & MOEGG_PERMUTE_Y;
     if (px && py)
-        return MOEGG_EINVAL;  // "Cannot permute both X and Y"
+        return MOEGG_EINVAL;  // the pages' launcher rejects both permutes at once
     if ((px || py) && S > 0 && gather_idx == nullptr)
         return MOEGG_EINVAL;  // gather_indices required with a permute flag
     return MOEGG_OK;
@@ -143,7 +143,7 @@ moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t 
     if ((st = check_permute_flags(flags, gather_idx, (int64_t)num_tokens * topk)) != MOEGG_OK)
         return st;
     if ((flags & MOEGG_FUSE_MUL_POST) && !(flags & MOEGG_PERMUTE_Y))
-        return MOEGG_EINVAL;  // "FUSE_MUL requires PERMUTE_Y"
+        return MOEGG_EINVAL;  // the gate multiply is fused only with permute_y
     if ((flags & MOEGG_FUSE_MUL_POST) && num_tokens > 0 && topk_weights == nullptr)
         return MOEGG_EINVAL;
     if (num_tokens == 0)
@@ -299,6 +299,77 @@ moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_gr
     if (device_cus(&cus) != 0)
         return MOEGG_EHIP;
     return from_hip(moegg::groups_launch(p, trans_b, cus, static_cast<hipStream_t>(stream)));
+}
+
+// Shared checks of the combine entry points.
+static moegg_status check_combine(int64_t num_tokens, int32_t topk, int32_t N, int64_t y_rows,
+                                  const int32_t *scatter)
+{
+    if (num_tokens < 0 || topk < 1 || N < 1 || N % 8 != 0 || y_rows < 0)
+        return MOEGG_ESHAPE;
+    if (num_tokens * topk > INT32_MAX)
+        return MOEGG_ESHAPE;
+    if (scatter == nullptr && y_rows < num_tokens * topk)
+        return MOEGG_ESHAPE;  // slot-order Y has one row per slot
+    if (y_rows * (int64_t)N * 2 >= ((int64_t)1 << 40) || num_tokens * (int64_t)N * 4 >= ((int64_t)1 << 40))
+        return MOEGG_ESHAPE;
+    return MOEGG_OK;
+}
+
+moegg_status moegg_combine(const void *Y, const int32_t *scatter_idx, const float *topk_weights,
+                           int64_t num_tokens, int32_t topk, int32_t N, int64_t y_rows,
+                           uint32_t flags, void *out, int32_t *error_flags, void *stream)
+{
+    moegg_status st = check_combine(num_tokens, topk, N, y_rows, scatter_idx);
+    if (st != MOEGG_OK)
+        return st;
+    if (flags & ~(uint32_t)MOEGG_COMBINE_FP32_OUT)
+        return MOEGG_EINVAL;
+    if (num_tokens == 0)
+        return MOEGG_OK;
+    if (!Y || !out || !aligned16(Y) || !aligned16(out))
+        return MOEGG_EINVAL;
+    moegg::CombineParams p;
+    p.Y = static_cast<const char *>(Y);
+    p.scatter = scatter_idx;
+    p.weights = topk_weights;
+    p.out = static_cast<char *>(out);
+    p.err = error_flags;
+    p.T = num_tokens;
+    p.y_rows = y_rows;
+    p.topk = topk;
+    p.N = N;
+    p.f32_out = flags & MOEGG_COMBINE_FP32_OUT;
+    return from_hip(moegg::combine_launch(p, static_cast<hipStream_t>(stream)));
+}
+
+moegg_status moegg_combine_bwd(const void *dOut, const void *Y, const int32_t *scatter_idx,
+                               const float *topk_weights, int64_t num_tokens, int32_t topk,
+                               int32_t N, int64_t y_rows, void *dY, float *dw,
+                               int32_t *error_flags, void *stream)
+{
+    moegg_status st = check_combine(num_tokens, topk, N, y_rows, scatter_idx);
+    if (st != MOEGG_OK)
+        return st;
+    if (num_tokens == 0)
+        return MOEGG_OK;
+    if (!dOut || !dY || !aligned16(dOut) || !aligned16(dY))
+        return MOEGG_EINVAL;
+    if (dw && (!Y || !aligned16(Y)))
+        return MOEGG_EINVAL;  // the weight gradient reads the forward input
+    moegg::CombineBwdParams p;
+    p.dOut = static_cast<const char *>(dOut);
+    p.Y = static_cast<const char *>(Y);
+    p.scatter = scatter_idx;
+    p.weights = topk_weights;
+    p.dY = static_cast<char *>(dY);
+    p.dw = dw;
+    p.err = error_flags;
+    p.T = num_tokens;
+    p.y_rows = y_rows;
+    p.topk = topk;
+    p.N = N;
+    return from_hip(moegg::combine_bwd_launch(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -788,6 +788,7 @@ __device__ __forceinline__ void quad_slot(const char *smem, int q, f32x16_t (&ac
     constexpr int HALF = Q::NCOPY / 2;
     const int cq = q + kSlots - 1, cbuf = cq % kSlots;
     __builtin_amdgcn_sched_barrier(0);
+    copy.phase_a(q);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
         quad_mma<PART>(t, f.a0, f.b0, acc, ib);
@@ -813,10 +814,13 @@ __device__ __forceinline__ void quad_slot(const char *smem, int q, f32x16_t (&ac
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    copy.phase_b_end(q);
 }
 
 // copy(q, buf, n): this wave's copy n (0 .. NCOPY-1) of reduction slot q into
-// slot buffer buf.
+// slot buffer buf.  Hooks (no-ops in PlainCopy): prepare(q) readies the row
+// offsets of slot q before its first copy (prologue); phase_a(q) and
+// phase_b_end(q) bracket slot q, for copiers that fetch row indices ahead.
 template <class C, bool PART, class Copy, class FA, class FB>
 __device__ __forceinline__ void quad_body(const char *smem, int nslots, f32x16_t (&acc)[4][4],
                                           Copy &copy, int ib, const FA &fa, const FB &fb)
@@ -831,10 +835,13 @@ __device__ __forceinline__ void quad_body(const char *smem, int nslots, f32x16_t
     __builtin_amdgcn_s_waitcnt(0);
     QuadFrags f;
     const int pre = min(kSlots - 1, nslots);
-    for (int q = 0; q < pre; ++q)
+    for (int q = 0; q < pre; ++q) {
+        copy.prepare(q);
 #pragma unroll
         for (int n = 0; n < N; ++n)
             copy(q, q, n);
+    }
+    copy.prepare(kSlots - 1);
     wait_batch<N>(pre - 1);
     wg_barrier();
 #pragma unroll
@@ -851,13 +858,28 @@ __device__ __forceinline__ void quad_body(const char *smem, int nslots, f32x16_t
     quad_slot<C, PART, false, false, 0>(smem, q, acc, f, copy, ib, fa, fb);
 }
 
+// A copy callback f(q, buf, n) without row-index prefetching.
+template <class F>
+struct PlainCopy {
+    F f;
+    __device__ __forceinline__ void operator()(int q, int buf, int n) { f(q, buf, n); }
+    __device__ __forceinline__ void prepare(int) {}
+    __device__ __forceinline__ void phase_a(int) {}
+    __device__ __forceinline__ void phase_b_end(int) {}
+};
+template <class F>
+__device__ __forceinline__ PlainCopy<F> plain_copy(F f)
+{
+    return PlainCopy<F>{f};
+}
+
 // A_TR / B_TR: operand layout (OpFrag).  rows: real rows of the tile (A
 // side); waves of a ragged tail skip the MFMAs and A reads of their padding
 // 32-row blocks but keep every barrier.  Leaves LDS free for the epilogue
 // (all reads and copies complete).
 template <class C, bool A_TR, bool B_TR, class Copy>
 __device__ __forceinline__ void mainloop_quad(const char *smem, int nslots,
-                                              f32x16_t (&acc)[C::FM][C::FN], Copy copy, int rows)
+                                              f32x16_t (&acc)[C::FM][C::FN], Copy &&copy, int rows)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -920,6 +942,12 @@ struct SlotTileCopier {
                       lds0 + (uint32_t)(slot * SLOT_BYTES + j * kWave * 16));
     }
 };
+
+// n / d for the divisor d described by FastDiv (exact for n < 2^31).
+__device__ __forceinline__ int fast_div(uint32_t n, FastDiv d)
+{
+    return (int)((__umulhi(n, d.mul) + n) >> d.shift);
+}
 
 // Row and column of accumulator element r of 32x32 block (i, j) for this lane.
 template <class C>
@@ -1225,12 +1253,12 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
             zero_acc<C>(acc);
             mainloop_quad<C, false, true>(
                 smem, (N + SK - 1) / SK, acc,
-                [&](int q, int buf, int n) {
+                plain_copy([&](int q, int buf, int n) {
                     if (n < Q::NCA)
                         ca.template issue_one<Q::SLOT>(dyr, n, buf, q * SK, N);
                     else
                         cb.template issue_one<Q::SLOT>(wr, n - Q::NCA, buf, q, N);
-                },
+                }),
                 rows);
             epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
             continue;
@@ -1285,18 +1313,14 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 
 constexpr int kGroupK = 8;
 
-__device__ __forceinline__ int fast_div(uint32_t n, FastDiv d)
-{
-    return (int)((__umulhi(n, d.mul) + n) >> d.shift);
-}
 
 // PX / PY: the forward's permute flags, as template parameters so that the
 // per-stage row-index code has no flag branches.
 template <class C, bool PX, bool PY>
 __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
 {
-    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
-    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+    char *const st0 = smem, *const st1 = smem + C::STAGE;
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_order[kMaxExperts];

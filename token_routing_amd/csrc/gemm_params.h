@@ -71,10 +71,38 @@ struct GroupsParams {
     int num;
 };
 
+// Top-k combine: out[t] = sum_j w[t*k+j] * Y[row(t*k+j)].
+struct CombineParams {
+    const char *Y;           // bf16 [y_rows, N]
+    const int32_t *scatter;  // slot -> row of Y, or null (Y in slot order)
+    const float *weights;    // [T*k] or null (1)
+    char *out;               // bf16 or fp32 [T, N]
+    int32_t *err;
+    int64_t T, y_rows;
+    int topk, N;
+    bool f32_out;
+};
+
+// Its backward: dY[row(s)] = w[s] * dOut[t], dw[s] = <dOut[t], Y[row(s)]>.
+struct CombineBwdParams {
+    const char *dOut;        // bf16 [T, N]
+    const char *Y;           // bf16 [y_rows, N] (read only when dw is requested)
+    const int32_t *scatter;
+    const float *weights;
+    char *dY;                // bf16 [y_rows, N]
+    float *dw;               // [T*k] or null
+    int32_t *err;
+    int64_t T, y_rows;
+    int topk, N;
+};
+
 hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream);
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream);
 hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream);
 hipError_t groups_launch(const GroupsParams &p, int trans_b, int cus, hipStream_t stream);
+
+hipError_t combine_launch(const CombineParams &p, hipStream_t stream);
+hipError_t combine_bwd_launch(const CombineBwdParams &p, hipStream_t stream);
 
 int64_t route_chunks(int64_t S);
 hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32_t *m_sizes,

@@ -44,7 +44,8 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp]
+            ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp,
+             "-lm"]
         )
         os.replace(tmp, _LIB)
     return _LIB
@@ -53,7 +54,9 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build(force=not os.path.exists(_LIB))
+        stale = (not os.path.exists(_LIB)
+                 or os.path.getmtime(_LIB) < os.path.getmtime(_SRC))
+        build(force=stale)
         lib = ctypes.CDLL(_LIB)
         vp = ctypes.c_void_p
         i32, i64, u32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
@@ -75,6 +78,8 @@ def _load():
         lib.oracle_combine.restype = None
         lib.oracle_combine_bwd.argtypes = [vp, vp, vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_combine_bwd.restype = None
+        lib.oracle_gated_silu.argtypes = [vp, i64, i32, vp]
+        lib.oracle_gated_silu.restype = None
         _lib = lib
     return _lib
 
@@ -234,3 +239,31 @@ def combine_bwd(dOut, Y, topk: int, scatter=None, weights=None):
     _load().oracle_combine_bwd(_ptr(dOut), _ptr(Y), _ptr(scatter), _ptr(weights), T, topk, N,
                                _ptr(dY), _ptr(dw))
     return dY, dw
+
+
+def gated_silu(A):
+    """Gated activation: out[:, c] = silu(A[:, 2c]) * A[:, 2c + 1] (double, rounded to fp32).
+
+    A: float32 [rows, N] with N even.  Returns float32 [rows, N // 2].
+    """
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    rows, N = A.shape
+    if N % 2:
+        raise ValueError("the gated activation needs an even number of columns")
+    out = np.zeros((rows, N // 2), np.float32)
+    _load().oracle_gated_silu(_ptr(A), rows, N, _ptr(out))
+    return out
+
+
+def grouped_gemm_fwd_gated(X, W, m_sizes, gather, topk: int, flags: int, rows=None, cols=None):
+    """The gate_up forward followed by the gated activation.
+
+    Output column c of the [S, N/2] result takes W rows 2c (gate) and 2c + 1
+    (linear) of its expert.  rows as in grouped_gemm_fwd; cols: output
+    columns in [0, N/2) (default all).  Returns float32 [len(rows), len(cols)].
+    """
+    N = int(W.shape[1])
+    oc = np.arange(N // 2, dtype=np.int64) if cols is None else np.asarray(cols, np.int64)
+    wc = np.stack([2 * oc, 2 * oc + 1], axis=1).reshape(-1)
+    A = grouped_gemm_fwd(X, W, m_sizes, gather, None, topk, flags, rows=rows, cols=wc)
+    return gated_silu(A)

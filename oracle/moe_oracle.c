@@ -22,6 +22,7 @@
  * nest its definition states.  Built with gcc -O2 and no -ffast-math, so the
  * compiler may not reassociate the fp32 sums.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -353,5 +354,26 @@ void oracle_combine_bwd(const uint16_t *dOut, const uint16_t *Y, const int32_t *
             }
             if (dw)
                 dw[s] = acc;
+        }
+}
+
+/*
+ * Gated activation on the output of the first (gate_up) GEMM: the
+ * FusedActivation of triton_kernels/matmul_ogs.py with reduction_n = 2,
+ * whose output keeps N / 2 columns.  The pages leave the function open; it
+ * is taken as the SiLU-gated unit of Mixtral-shaped experts, with the two
+ * columns that reduce into one output column adjacent, gate first:
+ *   out[r, c] = silu(A[r, 2c]) * A[r, 2c + 1],   silu(x) = x / (1 + exp(-x)),
+ * evaluated in double from the fp32 inputs and rounded once to fp32.
+ * A is [rows, N] fp32 with N even; out is [rows, N / 2].
+ */
+void oracle_gated_silu(const float *A, int64_t rows, int32_t N, float *out)
+{
+    int32_t H = N / 2;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t c = 0; c < H; ++c) {
+            double g = A[r * N + 2 * c];
+            double u = A[r * N + 2 * c + 1];
+            out[r * H + c] = (float)(g / (1.0 + exp(-g)) * u);
         }
 }

@@ -63,12 +63,17 @@ def _useful(m_sizes, N, K):
     return 2.0 * float(np.sum(m_sizes)) * N * K
 
 
-def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1):
-    """route + forward (+ dX + dW) of one routed grouped GEMM."""
+def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
+    """route + forward (+ dX + dW) of one routed grouped GEMM.
+
+    extra_flags = GATED_SILU: the gate_up forward with the activation fused
+    (output [S, N/2]); the backward is then not part of the step.
+    """
     st = Step(wl.name)
     E, N, K = wl.W.shape
     S, T, topk = wl.S, wl.T, wl.topk
-    flags = wl.flags
+    flags = wl.flags | extra_flags
+    out_cols = N // 2 if (flags & mg.GATED_SILU) else N
     ids = _dev(wl.ids)
     X = _dev(wl.X)
     Ws = [_dev(wl.W)]
@@ -80,7 +85,7 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1):
     torch.cuda.synchronize()
     m_sizes = route_out["m_sizes"].cpu().numpy()
     nonempty = int((m_sizes > 0).sum())
-    Y = torch.empty(S, N, dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty(S, out_cols, dtype=torch.bfloat16, device="cuda")
     it = {"i": 0}
 
     def route():
@@ -95,7 +100,7 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1):
     x_rows = T if (flags & synth.PERMUTE_X) else S
     st.add("route", route, 0.0, S * 4 * 3 + E * 4 * 4)
     st.add("fwd", fwd, _useful(m_sizes, N, K),
-           nonempty * N * K * 2 + x_rows * K * 2 + S * N * 2 + S * 4 * 2)
+           nonempty * N * K * 2 + x_rows * K * 2 + S * out_cols * 2 + S * 4 * 2)
     if with_bwd:
         bwd_flags = flags & (synth.PERMUTE_X | synth.PERMUTE_Y)
         dY = synth.normal_bf16((S, N), 0.01, synth.generator(dY_seed)).to("cuda")
@@ -113,6 +118,7 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1):
         st.add("dX", bwd_dx, _useful(m_sizes, N, K), S * N * 2 + nonempty * N * K * 2 + S * K * 2)
         st.add("dW", bwd_dw, _useful(m_sizes, N, K), S * N * 2 + x_rows * K * 2 + E * N * K * 2)
     st.m_sizes = m_sizes
+    st.flags = flags
     st.inputs = wl
     return st
 
@@ -170,6 +176,9 @@ def build_combine_step(wl, rotate=2):
 def make_step(name):
     if name == "mixtral":
         return build_layer_step(synth.mixtral(), dY_seed=synth.SEEDS["mixtral_bwd_dy"])
+    if name == "mixtral_gated":
+        return build_layer_step(synth.mixtral(), dY_seed=0, with_bwd=False,
+                                extra_flags=mg.GATED_SILU)
     if name == "fine":
         return build_layer_step(synth.fine_bwd(), dY_seed=synth.SEEDS["fine_bwd_dy"])
     if name == "fine_fwd":
@@ -188,6 +197,9 @@ def make_step(name):
 WORKLOAD_DESC = {
     "mixtral": "Mixtral-shaped MoE gate_up grouped GEMM, T=4096 K=4096 N=28672 E=8 top-2, "
                "permute_x; step = route + fwd + dX + dW",
+    "mixtral_gated": "Mixtral-shaped MoE gate_up grouped GEMM with the gated SiLU fused in the "
+                     "epilogue, T=4096 K=4096 N=28672 (-> 14336) E=8 top-2, permute_x; "
+                     "step = route + fwd",
     "fine": "fine-grained MoE down grouped GEMM, T=8192 E=128 top-8 K=768 N=2048 Zipf(1.2); "
             "step = route + fwd(permute_y+fuse_mul_post) + dX + dW",
     "fine_fwd": "fine-grained MoE down grouped GEMM forward, T=8192 E=128 top-8 K=768 N=2048",
@@ -225,9 +237,19 @@ def time_step(st, steps, warmup):
     return per / steps, total / steps, wall
 
 
-def kernel_source_sha():
+def kernel_source_sha(label=None):
+    """sha256[:16] of the sources a kernel is built from (all kernels' when
+    label is None): the shared headers plus the kernel's own file."""
+    if label is None:
+        own = ("gemm.hip", "route.hip", "combine.hip")
+    elif label.startswith("combine"):
+        own = ("combine.hip",)
+    elif label.startswith("route"):
+        own = ("route.hip",)
+    else:
+        own = ("gemm.hip",)
     h = hashlib.sha256()
-    for f in ("gemm.hip", "route.hip", "common.h", "gemm_params.h"):
+    for f in own + ("common.h", "gemm_params.h"):
         with open(os.path.join(ROOT, "token_routing_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -240,7 +262,7 @@ def measured_traffic(workload, label):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_src_sha") != kernel_source_sha():
+    if rec.get("kernel_src_sha") != kernel_source_sha(label):
         return None
     return rec.get("bytes_per_launch")
 
@@ -293,20 +315,27 @@ def cpu_baseline(st, budget_s):
     rng = np.random.default_rng(0)
     per_row = 2.0 * N * K
 
+    gated = bool(st.flags & mg.GATED_SILU)
+
     def run(nrows):
         rows = rng.choice(wl.S, size=min(nrows, wl.S), replace=False)
         if wl.flags & synth.PERMUTE_Y:
             rows = ref_route["gather"][rows]     # output rows are slots
         t = time.perf_counter()
-        oracle.grouped_gemm_fwd(Xb, Wb, ref_route["m_sizes"], ref_route["gather"], gate,
-                                wl.topk, wl.flags, rows=rows)
+        if gated:
+            oracle.grouped_gemm_fwd_gated(Xb, Wb, ref_route["m_sizes"], ref_route["gather"],
+                                          wl.topk, wl.flags, rows=rows)
+        else:
+            oracle.grouped_gemm_fwd(Xb, Wb, ref_route["m_sizes"], ref_route["gather"], gate,
+                                    wl.topk, wl.flags, rows=rows)
         return len(rows), time.perf_counter() - t
 
     n1, t1 = run(2)
     n, dt = run(max(1, int(budget_s / max(t1 / n1, 1e-9))))
     return {"value": per_row * n / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "sample": f"routing of all {wl.S} slots ({t_route:.3f} s) + forward of {n} random "
-                      f"output rows x all {N} columns (K={K}); the oracle's rate on them",
+                      f"output rows x all {N} columns (K={K})"
+                      f"{' and their gated activation' if gated else ''}; the oracle's rate on them",
             "seconds": round(dt, 3)}
 
 
@@ -390,7 +419,7 @@ def summarize(prof_dir, workload, command):
             rd = fetch[lab] * 1024 * cal["FETCH_SIZE"]
             wr = write[lab] * 1024 * cal["WRITE_SIZE"]
             lines.append(f"| {lab} | {rd / 1e6:.1f} | {wr / 1e6:.1f} |")
-            json.dump({"kernel_src_sha": sha, "workload": workload, "kernel": lab,
+            json.dump({"kernel_src_sha": kernel_source_sha(lab), "workload": workload, "kernel": lab,
                        "bytes_per_launch": round(rd + wr), "read_bytes": round(rd),
                        "write_bytes": round(wr), "fetch_scale": cal["FETCH_SIZE"],
                        "write_scale": cal["WRITE_SIZE"]},
@@ -406,7 +435,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # MI355X raises its clock over the first tens of milliseconds of MFMA load:
+    # 3 warmup steps of the gated gate_up forward time it 5% slower than 30.
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for the baseline (0 disables)")

@@ -58,6 +58,7 @@ typedef enum {
 #define MOEGG_PERMUTE_Y 2u     /* scatter output rows back to slot order on store */
 #define MOEGG_FUSE_MUL_POST 4u /* multiply each output row by its gate weight     */
 #define MOEGG_DW_FP32_OUT 8u   /* dW only: write fp32 instead of bf16             */
+#define MOEGG_GATED_SILU 32u   /* forward only: gated SiLU on (gate, linear) pairs */
 
 /* Device error bits ORed into *error_flags. */
 #define MOEGG_DERR_EXPERT_ID 1 /* a top-k expert id outside [0, E): slot dropped  */
@@ -129,6 +130,14 @@ moegg_status moegg_route(const int32_t *topk_ids, int32_t num_tokens, int32_t to
  *            slot, topk_weights is [S] in slot order);
  *   stored as bf16 (round to nearest even) to row gather_idx[p] of Y with
  *   MOEGG_PERMUTE_Y, else to row p.  Y is [S, N].
+ *   MOEGG_GATED_SILU: the gate_up GEMM with its activation fused (the
+ *            FusedActivation of triton_kernels/matmul_ogs.py with
+ *            reduction_n = 2, output width N/2).  W rows come in adjacent
+ *            (gate, linear) pairs and
+ *              out[c] = silu(y[2c]) * y[2c + 1],  silu(x) = x / (1 + e^-x),
+ *            from the fp32 accumulators, rounded once to bf16.  Y is
+ *            [S, N/2].  Not with PERMUTE_Y or FUSE_MUL_POST (the activation
+ *            belongs to the first GEMM); N must be a multiple of 16.
  *
  *   m_sizes     [E] device int32 rows per expert (moegg_route output); read
  *               on the device, no host synchronisation.
@@ -136,9 +145,11 @@ moegg_status moegg_route(const int32_t *topk_ids, int32_t num_tokens, int32_t to
  *   error_flags optional device int32 (see Errors above).
  *
  * Errors: EINVAL if both permute flags are set, FUSE_MUL_POST without
- * PERMUTE_Y, or a required pointer is NULL (gather_idx with a permute flag,
- * topk_weights with FUSE_MUL_POST); ESHAPE for non-positive sizes, K or N
- * not a multiple of 8, E > MOEGG_MAX_EXPERTS.  T = 0 is a no-op.
+ * PERMUTE_Y, GATED_SILU with PERMUTE_Y or FUSE_MUL_POST, an unknown flag, or
+ * a required pointer is NULL (gather_idx with a permute flag, topk_weights
+ * with FUSE_MUL_POST); ESHAPE for non-positive sizes, K or N not a multiple
+ * of 8 (of 16 for N with GATED_SILU), E > MOEGG_MAX_EXPERTS.  T = 0 is a
+ * no-op.
  */
 moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t *m_sizes,
                                     const int32_t *gather_idx, const float *topk_weights,

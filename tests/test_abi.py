@@ -48,7 +48,7 @@ def test_route_workspace_size(lib):
 
 
 EINVAL, ESHAPE, EUNSUP, EWS = 1, 2, 3, 4
-PX, PY, FM, F32 = 1, 2, 4, 8
+PX, PY, FM, F32, GS = 1, 2, 4, 8, 32
 FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every case fails on the host
 
 
@@ -57,6 +57,9 @@ FAKE = ctypes.c_void_p(1 << 20)  # never dereferenced: every case fails on the h
     (FM, EINVAL),             # fuse_mul_post requires permute_y
     (PX | FM, EINVAL),
     (16, EINVAL),             # unknown flag
+    (64, EINVAL),
+    (GS | PY, EINVAL),        # the gated activation belongs to the first GEMM
+    (GS | PY | FM, EINVAL),
 ])
 def test_fwd_flag_checks(lib, flags, want):
     st = lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, flags, FAKE,
@@ -78,6 +81,17 @@ def test_fwd_missing_pointers(lib):
 def test_fwd_shape_checks(lib, T, k, E, N, K):
     assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, T, k, E, N, K, 0, FAKE, None,
                                       None) == ESHAPE
+
+
+def test_gated_shape_and_backward_checks(lib):
+    # N/2 output columns must be whole 16-byte segments
+    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 40, 64, GS | PX,
+                                      FAKE, None, None) == ESHAPE
+    # the backward kernels take no activation flag
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None,
+                                     None) == EINVAL
+    assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None,
+                                     None) == EINVAL
 
 
 def test_operand_size_limit(lib):

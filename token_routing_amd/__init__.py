@@ -21,6 +21,7 @@ PERMUTE_X = 1
 PERMUTE_Y = 2
 FUSE_MUL_POST = 4
 DW_FP32_OUT = 8
+GATED_SILU = 32
 
 DERR_EXPERT_ID = 1
 DERR_M_SIZES = 2
@@ -156,14 +157,16 @@ def grouped_gemm_fwd(X, W, m_sizes, gather_idx, topk_weights, topk: int, flags: 
 
     X: bf16 [T, K] (PERMUTE_X) or [T*topk, K]; W: bf16 [E, N, K]; m_sizes int32
     [E]; gather_idx int32 [T*topk]; topk_weights fp32 [T*topk] (slot order).
-    Returns Y bf16 [T*topk, N].
+    Returns Y bf16 [T*topk, N], or [T*topk, N/2] with GATED_SILU (W rows in
+    (gate, linear) pairs).
     """
     lib = load_library()
     E, N, K = W.shape
     S = gather_idx.numel() if gather_idx is not None else X.shape[0]
     T = S // topk
     if Y is None:
-        Y = torch.empty(S, N, dtype=torch.bfloat16, device=X.device)
+        Y = torch.empty(S, N // 2 if (flags & GATED_SILU) else N, dtype=torch.bfloat16,
+                        device=X.device)
     _check(lib.moegg_grouped_gemm_fwd(
         _ptr(_device_tensor(X, torch.bfloat16, "X")), _ptr(_device_tensor(W, torch.bfloat16, "W")),
         _ptr(_device_tensor(m_sizes, torch.int32, "m_sizes")),

@@ -138,12 +138,16 @@ moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t 
     moegg_status st = check_gemm_common(num_tokens, topk, num_experts, N, K);
     if (st != MOEGG_OK)
         return st;
-    if (flags & ~(MOEGG_PERMUTE_X | MOEGG_PERMUTE_Y | MOEGG_FUSE_MUL_POST))
+    if (flags & ~(MOEGG_PERMUTE_X | MOEGG_PERMUTE_Y | MOEGG_FUSE_MUL_POST | MOEGG_GATED_SILU))
         return MOEGG_EINVAL;
     if ((st = check_permute_flags(flags, gather_idx, (int64_t)num_tokens * topk)) != MOEGG_OK)
         return st;
     if ((flags & MOEGG_FUSE_MUL_POST) && !(flags & MOEGG_PERMUTE_Y))
         return MOEGG_EINVAL;  // the gate multiply is fused only with permute_y
+    if ((flags & MOEGG_GATED_SILU) && (flags & (MOEGG_PERMUTE_Y | MOEGG_FUSE_MUL_POST)))
+        return MOEGG_EINVAL;  // the activation belongs to the first GEMM
+    if ((flags & MOEGG_GATED_SILU) && N % 16 != 0)
+        return MOEGG_ESHAPE;  // N/2 output columns in 16-byte segments
     if ((flags & MOEGG_FUSE_MUL_POST) && num_tokens > 0 && topk_weights == nullptr)
         return MOEGG_EINVAL;
     if (num_tokens == 0)

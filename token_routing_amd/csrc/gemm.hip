@@ -1051,6 +1051,67 @@ __device__ __forceinline__ void epilogue_f32(const f32x16_t (&acc)[C::FM][C::FN]
             }
 }
 
+// Gated activation on the gate_up output (reduction_n = 2): output column c
+// is silu(A[:, 2c]) * A[:, 2c + 1].  The W tile is loaded with its rows
+// permuted (gated_row) so that a lane's accumulator block j < FN/2 holds the
+// gate and block j + FN/2 the linear partner of the same output column in the
+// same register: the activation needs no data exchange between lanes.
+//
+// Tile row r (wave column wn = r / TN, block j, lane l = r % 32) holds W row
+// n0 + 2 * (wn * TN/2 + (j mod FN/2) * 32 + l) + (j >= FN/2): a bijection of
+// [0, BN) onto itself, and output column n0/2 + wn * TN/2 + (j mod FN/2) * 32 + l.
+template <class C>
+__device__ __forceinline__ int gated_row(int r)
+{
+    static_assert(C::FN % 2 == 0, "the gated epilogue pairs accumulator blocks");
+    constexpr int H = C::FN / 2;
+    const int wn = r / C::TN, j = (r % C::TN) / 32, l = r % 32;
+    return 2 * (wn * (C::TN / 2) + (j % H) * 32 + l) + j / H;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// Stages the BM x BN/2 bf16 output tile in st0 and copies it out as 16-byte
+// row segments to Y (leading dimension ldy, tile column c -> o0 + c, valid
+// below ncols), like epilogue_bf16.
+template <class C>
+__device__ __forceinline__ void epilogue_gated(char *st0, const f32x16_t (&acc)[C::FM][C::FN],
+                                               const int *s_dst, char *Y, int64_t ldy, int o0,
+                                               int ncols)
+{
+    constexpr int OC = C::BN / 2, H = C::FN / 2;
+    static_assert(C::BM * OC * 2 <= C::STAGE, "the gated tile fits in one stage");
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int row0 = wm * C::TM + 4 * (lane >> 5);
+    uint16_t *base = reinterpret_cast<uint16_t *>(st0) + row0 * OC + wn * (C::TN / 2) + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int rr = i * 32 + 8 * (r >> 2) + (r & 3);
+#pragma unroll
+            for (int j = 0; j < H; ++j)
+                base[rr * OC + j * 32] = to_bf16(silu_mul(acc[i][j][r], acc[i][j + H][r]));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    __syncthreads();
+    constexpr int CPR = OC / 8;
+    for (int idx = threadIdx.x; idx < C::BM * CPR; idx += C::NT) {
+        const int row = idx / CPR, ch = idx % CPR;
+        const int dst = s_dst[row];
+        const int col = o0 + ch * 8;
+        if (dst >= 0 && col < ncols)
+            *reinterpret_cast<uint4 *>(Y + ((int64_t)dst * ldy + col) * 2) =
+                *reinterpret_cast<const uint4 *>(st0 + (row * OC + ch * 8) * 2);
+    }
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Expert tables shared by the routed kernels
 // ---------------------------------------------------------------------------
@@ -1104,7 +1165,9 @@ __device__ __forceinline__ int checked_gather(const int32_t *gather, int64_t p, 
 // Forward
 // ---------------------------------------------------------------------------
 
-template <class C>
+// GATED: W rows come in (gate, linear) pairs and Y gets N/2 columns of the
+// gated activation (epilogue_gated).
+template <class C, bool GATED>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 {
     __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
@@ -1168,7 +1231,10 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 #pragma unroll
         for (int i = 0; i < lb.RPT; ++i) {
             const int r = lb.tile_row(i);
-            lb.set_row(i, n0 + r < a.N ? n0 + r : -1, row_bytes);
+            int wrow = n0 + r;
+            if constexpr (GATED)
+                wrow = n0 + gated_row<C>(r);
+            lb.set_row(i, wrow < a.N ? wrow : -1, row_bytes);
         }
         mainloop<C, true, false, false>(
             st0, st1, nsteps, acc,
@@ -1181,7 +1247,10 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
                 lb.store(Bs);
             },
             rows);
-        epilogue_bf16<C, true>(st0, st1, acc, s_dst, s_scale, a.Y, a.N, n0, a.N);
+        if constexpr (GATED)
+            epilogue_gated<C>(st0, acc, s_dst, a.Y, a.N / 2, n0 / 2, a.N / 2);
+        else
+            epilogue_bf16<C, true>(st0, st1, acc, s_dst, s_scale, a.Y, a.N, n0, a.N);
     }
 }
 
@@ -1582,11 +1651,14 @@ using DxCfg = Cfg<MOEGG_DX_CFG>;
 using DxQuadCfg = Cfg<256, 256, 2, 2>;  // long reductions: four-wave engine
 using DwCfg = Cfg<MOEGG_DW_CFG>;
 using SmallCfg = Cfg<MOEGG_SMALL_CFG>;   // few rows per expert: stream the weights
+using SmallGatedCfg = Cfg<32, 256, 1, 4>;  // the same with two blocks per wave to pair
 using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
 
 // Explicit instantiations: every kernel the launchers use is emitted here.
-template __global__ void fwd_kernel<BigCfg>(FwdParams);
-template __global__ void fwd_kernel<SmallCfg>(FwdParams);
+template __global__ void fwd_kernel<BigCfg, false>(FwdParams);
+template __global__ void fwd_kernel<SmallCfg, false>(FwdParams);
+template __global__ void fwd_kernel<BigCfg, true>(FwdParams);
+template __global__ void fwd_kernel<SmallGatedCfg, true>(FwdParams);
 template __global__ void dx_kernel<DxCfg>(DxParams);
 template __global__ void dx_kernel<DxQuadCfg>(DxParams);
 template __global__ void dw_kernel<DwCfg, false, false>(DwParams);
@@ -1619,19 +1691,28 @@ static int grid_for(int64_t tiles_bound, int cus, int resident)
     return (int)(g < 1 ? 1 : g);
 }
 
+template <class C, bool GATED>
+static void fwd_launch_cfg(const FwdParams &p, int cus, hipStream_t stream)
+{
+    const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.N + C::BN - 1) / C::BN);
+    static int res = resident_blocks(fwd_kernel<C, GATED>, C::NT);
+    hipLaunchKernelGGL((fwd_kernel<C, GATED>), dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0,
+                       stream, p);
+}
+
 hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream)
 {
-    const int64_t avg_rows = p.S / p.E;
-    if (avg_rows < 96) {
-        using C = SmallCfg;
-        const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.N + C::BN - 1) / C::BN);
-        static int res = resident_blocks(fwd_kernel<C>, C::NT);
-        hipLaunchKernelGGL(fwd_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    const bool small = p.S / p.E < 96;
+    if (p.flags & MOEGG_GATED_SILU) {
+        if (small)
+            fwd_launch_cfg<SmallGatedCfg, true>(p, cus, stream);
+        else
+            fwd_launch_cfg<BigCfg, true>(p, cus, stream);
     } else {
-        using C = BigCfg;
-        const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.N + C::BN - 1) / C::BN);
-        static int res = resident_blocks(fwd_kernel<C>, C::NT);
-        hipLaunchKernelGGL(fwd_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+        if (small)
+            fwd_launch_cfg<SmallCfg, false>(p, cus, stream);
+        else
+            fwd_launch_cfg<BigCfg, false>(p, cus, stream);
     }
     return hipGetLastError();
 }

@@ -106,6 +106,8 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
         dY = synth.normal_bf16((S, N), 0.01, synth.generator(dY_seed)).to("cuda")
         dX = torch.empty(S, K, dtype=torch.bfloat16, device="cuda")
         dW = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
+        ws_bytes = mg.dw_workspace_bytes(T, topk, E, N, K)
+        dw_ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
         def bwd_dx():
             mg.grouped_gemm_dX(dY, Ws[0], route_out["m_sizes"], route_out["gather"], topk,
@@ -113,7 +115,7 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
 
         def bwd_dw():
             mg.grouped_gemm_dW(X, dY, route_out["m_sizes"], route_out["gather"], topk, bwd_flags,
-                               dW=dW)
+                               dW=dW, workspace=dw_ws, split=dw_ws is not None)
 
         st.add("dX", bwd_dx, _useful(m_sizes, N, K), S * N * 2 + nonempty * N * K * 2 + S * K * 2)
         st.add("dW", bwd_dw, _useful(m_sizes, N, K), S * N * 2 + x_rows * K * 2 + E * N * K * 2)
@@ -354,6 +356,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
                  ("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
+                 ("dw_reduce_kernel", "dW_reduce"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),
                  ("route_scan", "route_scan"), ("route_scatter", "route_scatter"))
 

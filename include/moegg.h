@@ -189,12 +189,37 @@ moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t 
  *   (X is [S, K]); q(p) = gather_idx[p] with PERMUTE_Y, else p.
  * dW is [E, N, K], bf16, or fp32 with MOEGG_DW_FP32_OUT.  Experts with no
  * rows get exact zeros.
- * Errors: as for dX.
+ *
+ * Split reduction (the split-k of triton_kernels/matmul_ogs.py, whose fp32
+ * partials a separate reduce sums, applied to the rows of hot experts):
+ * with a workspace, an expert holding many more rows than the average is
+ * cut into chunks of rows whose fp32 partial products go to the workspace;
+ * a second launch on the same stream sums each expert's partials in chunk
+ * order and writes its dW.  The result is deterministic (the same for every
+ * run with the same inputs and workspace size), and differs from the
+ * unsplit sum only by fp32 rounding order.
+ *   workspace       device, 16-byte aligned, of at least
+ *                   moegg_grouped_gemm_dW_workspace_bytes(...) bytes
+ *                   (contents need no initialisation), or NULL: no split.
+ *   workspace_bytes its size; 0 with NULL.
+ * Errors: as for dX; EWORKSPACE if a workspace is given but smaller than
+ * needed.
  */
 moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t *m_sizes,
                                    const int32_t *gather_idx, int32_t num_tokens, int32_t topk,
                                    int32_t num_experts, int32_t N, int32_t K, uint32_t flags,
-                                   void *dW, int32_t *error_flags, void *stream);
+                                   void *dW, void *workspace, size_t workspace_bytes,
+                                   int32_t *error_flags, void *stream);
+
+/*
+ * Bytes of workspace moegg_grouped_gemm_dW can use to split hot experts'
+ * reductions, for these sizes: a small header plus fp32 [N, K] partials for
+ * fewer than 2 S / split_rows chunks, where split_rows is about
+ * S * ceil(N/256) * ceil(K/256) / 768 rows (at least 256).  0 when no
+ * expert can hold more than split_rows rows (then the workspace is unused).
+ */
+size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
+                                             int32_t num_experts, int32_t N, int32_t K);
 
 /*
  * One GEMM group: y[m, n] = x[m, k] @ w, bf16 in, fp32 accumulation, bf16 out.

@@ -91,7 +91,21 @@ def test_gated_shape_and_backward_checks(lib):
     assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None,
                                      None) == EINVAL
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None,
-                                     None) == EINVAL
+                                     0, None, None) == EINVAL
+
+
+def test_dw_workspace(lib):
+    # fine-grained layer: 65536 slots, 2048 x 768 per expert -> chunks of 2048 rows,
+    # fewer than 64 partials of 2048 x 768 fp32 after a 256-byte-aligned header
+    hdr = (4 + 12 * 128 + 255) // 256 * 256
+    assert lib.moegg_grouped_gemm_dW_workspace_bytes(8192, 8, 128, 2048, 768) == \
+        hdr + 64 * 2048 * 768 * 4
+    # Mixtral-shaped layer: an expert can never exceed the chunk length
+    assert lib.moegg_grouped_gemm_dW_workspace_bytes(4096, 2, 8, 28672, 4096) == 0
+    assert lib.moegg_grouped_gemm_dW_workspace_bytes(-1, 2, 8, 64, 64) == 0
+    # a workspace smaller than needed is rejected before anything runs
+    assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 8192, 8, 128, 2048, 768, PY, FAKE,
+                                     FAKE, 1024, None, None) == EWS
 
 
 def test_operand_size_limit(lib):
@@ -104,11 +118,11 @@ def test_backward_rejects_fuse_mul(lib):
     assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None,
                                      None) == EUNSUP
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None,
-                                     None) == EUNSUP
+                                     0, None, None) == EUNSUP
     assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, PX | PY, FAKE,
                                      None, None) == EINVAL
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, None, 10, 2, 8, 64, 64, PY, FAKE, None,
-                                     None) == EINVAL
+                                     0, None, None) == EINVAL
     assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, F32, FAKE, None,
                                      None) == EINVAL
 

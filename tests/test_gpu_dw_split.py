@@ -1,0 +1,123 @@
+"""GPU parity of dW with hot experts' reductions split into chunks.
+
+With a workspace, moegg_grouped_gemm_dW cuts every expert holding more than
+split_rows rows into chunks whose fp32 partials a second launch sums in chunk
+order.  Checked against the oracle (the unsplit definition) to the bf16
+tolerance and, for fp32 output, to 1e-5 relative Frobenius; against the
+unsplit GPU result; for bit-identical repeats; with empty experts; and with
+a workspace reused by a second, smaller call.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._util import bf16_tolerance_ok
+
+pytestmark = pytest.mark.gpu
+
+PX, PY = synth.PERMUTE_X, synth.PERMUTE_Y
+
+
+@pytest.fixture(scope="module")
+def mg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import token_routing_amd as mg
+    mg.load_library()
+    return mg
+
+
+def _split_rows(S, N, K):
+    """The chunk length the library documents: about S * tiles / 768 rows, a
+    multiple of 64, at least 256."""
+    tiles = -(-N // 256) * -(-K // 256)
+    rows = -(-S * tiles // 768)
+    return max(256, -(-rows // 64) * 64)
+
+
+def _hot_case(T, K, N, E, topk, flags, seed, s=2.0, n_never=1):
+    """Zipf routing with a steep exponent: a few experts hold most rows."""
+    g = synth.generator(seed)
+    rank = synth.zipf_rank(E, g)
+    ids, w = synth.route_zipf(T, E, topk, s, rank, g, n_never=n_never)
+    rows = T if (flags & PX) else T * topk
+    X = synth.normal_bf16((rows, K), 1.0, g)
+    W = synth.normal_bf16((E, N, K), 0.05, g)
+    dY = synth.normal_bf16((T * topk, N), 0.05, g)
+    return synth.Workload(f"hot_{seed}", T, K, N, E, topk, flags, ids, w, X, W, dY)
+
+
+def _dw(mg, wl, flags, **kw):
+    r = mg.moe_route(wl.ids.to("cuda"), wl.E, 128)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dW = mg.grouped_gemm_dW(wl.X.to("cuda"), wl.dY.to("cuda"), r["m_sizes"], r["gather"],
+                            wl.topk, flags, error_flags=err, **kw)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return dW
+
+
+def _oracle_dw(wl, flags):
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    E, N, K = wl.W.shape
+    ref = oracle.grouped_gemm_dW(synth.bits(wl.X), synth.bits(wl.dY), ref_route["m_sizes"],
+                                 ref_route["gather"], wl.topk, flags, E)
+    return ref.reshape(E, N, K), ref_route["m_sizes"]
+
+
+HOT = [
+    # T, K, N, E, topk, seed -- tails in N and K, one expert far above split_rows
+    (1200, 136, 264, 6, 2, 51),
+    (900, 320, 520, 10, 3, 52),
+]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])
+@pytest.mark.parametrize("case", HOT, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in HOT])
+def test_split_dw_matches_oracle(mg, flags, case):
+    T, K, N, E, topk, seed = case
+    wl = _hot_case(T, K, N, E, topk, flags, seed)
+    ref, m_sizes = _oracle_dw(wl, flags)
+    rows = _split_rows(wl.S, N, K)
+    assert m_sizes.max() > 3 * rows, "the case must split an expert into several chunks"
+    assert mg.dw_workspace_bytes(T, topk, E, N, K) > 0
+    dW = _dw(mg, wl, flags)
+    ok, info = bf16_tolerance_ok(dW.float().cpu().numpy().reshape(E * N, K),
+                                 ref.reshape(E * N, K))
+    print(f"split dW {case} flags={flags}: {info}", flush=True)
+    assert ok, info
+    for e in np.nonzero(m_sizes == 0)[0]:
+        assert torch.count_nonzero(dW[int(e)]).item() == 0
+    # the unsplit path agrees to the same bar
+    plain = _dw(mg, wl, flags, split=False)
+    ok, info = bf16_tolerance_ok(dW.float().cpu().numpy(), plain.float().cpu().numpy())
+    assert ok, info
+
+
+def test_split_dw_fp32_out_and_repeat(mg):
+    wl = _hot_case(1200, 136, 264, 6, 2, PY, 53)
+    ref, _ = _oracle_dw(wl, PY)
+    a = _dw(mg, wl, PY | mg.DW_FP32_OUT)
+    b = _dw(mg, wl, PY | mg.DW_FP32_OUT)
+    assert a.dtype == torch.float32
+    assert torch.equal(a, b), "split reduction must be deterministic"
+    ok, info = bf16_tolerance_ok(a.cpu().numpy().reshape(-1, 136), ref.reshape(-1, 136),
+                                 rel_fro_max=1e-5, max_elem=1e-4)
+    assert ok, info
+
+
+def test_split_workspace_reused_by_smaller_call(mg):
+    big = _hot_case(1200, 136, 264, 6, 2, PX, 54)
+    small = _hot_case(500, 136, 264, 6, 2, PX, 55)
+    ws = torch.empty(mg.dw_workspace_bytes(big.T, 2, 6, 264, 136), dtype=torch.uint8,
+                     device="cuda")
+    assert ws.numel() >= mg.dw_workspace_bytes(small.T, 2, 6, 264, 136) > 0
+    for wl in (big, small):
+        ref, _ = _oracle_dw(wl, PX)
+        dW = _dw(mg, wl, PX, workspace=ws)
+        ok, info = bf16_tolerance_ok(dW.float().cpu().numpy().reshape(-1, 136),
+                                     ref.reshape(-1, 136))
+        assert ok, (wl.name, info)

@@ -74,8 +74,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moegg_grouped_gemm_fwd.restype = ctypes.c_int
     lib.moegg_grouped_gemm_dX.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp, vp, vp]
     lib.moegg_grouped_gemm_dX.restype = ctypes.c_int
-    lib.moegg_grouped_gemm_dW.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp, vp, vp]
+    lib.moegg_grouped_gemm_dW.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp, vp,
+                                          sz, vp, vp]
     lib.moegg_grouped_gemm_dW.restype = ctypes.c_int
+    lib.moegg_grouped_gemm_dW_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.moegg_grouped_gemm_dW_workspace_bytes.restype = sz
     lib.moegg_grouped_gemm_groups.argtypes = [ctypes.POINTER(MoeggGroup), i32, i32, vp]
     lib.moegg_grouped_gemm_groups.restype = ctypes.c_int
     lib.moegg_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, u32, vp, vp, vp]
@@ -194,9 +197,20 @@ def grouped_gemm_dX(dY, W, m_sizes, gather_idx, topk: int, flags: int, *, dX=Non
     return dX
 
 
+def dw_workspace_bytes(num_tokens: int, topk: int, num_experts: int, N: int, K: int) -> int:
+    """Workspace bytes that let grouped_gemm_dW split hot experts' reductions (0: none)."""
+    return int(load_library().moegg_grouped_gemm_dW_workspace_bytes(num_tokens, topk,
+                                                                       num_experts, N, K))
+
+
 def grouped_gemm_dW(X, dY, m_sizes, gather_idx, topk: int, flags: int, *, dW=None,
-                    error_flags=None, stream=None):
-    """dW[e] = dY_e^T X_e (ragged per expert). Returns [E, N, K] bf16 (fp32 with DW_FP32_OUT)."""
+                    workspace=None, split: bool = True, error_flags=None, stream=None):
+    """dW[e] = dY_e^T X_e (ragged per expert). Returns [E, N, K] bf16 (fp32 with DW_FP32_OUT).
+
+    split: let the library cut hot experts' reductions into chunks (fp32
+    partials in `workspace`, a uint8 CUDA tensor of dw_workspace_bytes(...)
+    bytes, allocated here when not given).  split=False passes no workspace.
+    """
     lib = load_library()
     S, N = dY.shape
     K = X.shape[1]
@@ -204,11 +218,22 @@ def grouped_gemm_dW(X, dY, m_sizes, gather_idx, topk: int, flags: int, *, dW=Non
     if dW is None:
         dt = torch.float32 if (flags & DW_FP32_OUT) else torch.bfloat16
         dW = torch.empty(E, N, K, dtype=dt, device=dY.device)
+    ws_bytes = 0
+    if not split:
+        workspace = None
+    elif workspace is None:
+        need = dw_workspace_bytes(S // topk, topk, E, N, K)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dY.device)
+    if workspace is not None:
+        workspace = _device_tensor(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
     _check(lib.moegg_grouped_gemm_dW(
         _ptr(_device_tensor(X, torch.bfloat16, "X")), _ptr(_device_tensor(dY, torch.bfloat16, "dY")),
         _ptr(_device_tensor(m_sizes, torch.int32, "m_sizes")),
         _ptr(_device_tensor(gather_idx, torch.int32, "gather_idx")), S // topk, topk, E, N, K,
-        int(flags), _ptr(dW), _ptr(error_flags), _stream(stream)), "moegg_grouped_gemm_dW")
+        int(flags), _ptr(dW), _ptr(workspace), ws_bytes, _ptr(error_flags), _stream(stream)),
+        "moegg_grouped_gemm_dW")
     return dW
 
 

@@ -226,7 +226,8 @@ moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t 
 moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t *m_sizes,
                                    const int32_t *gather_idx, int32_t num_tokens, int32_t topk,
                                    int32_t num_experts, int32_t N, int32_t K, uint32_t flags,
-                                   void *dW, int32_t *error_flags, void *stream)
+                                   void *dW, void *workspace, size_t workspace_bytes,
+                                   int32_t *error_flags, void *stream)
 {
     moegg_status st = check_gemm_common(num_tokens, topk, num_experts, N, K);
     if (st != MOEGG_OK)
@@ -241,7 +242,7 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
         return MOEGG_EINVAL;
     if (num_tokens > 0 && (X == nullptr || dY == nullptr))
         return MOEGG_EINVAL;
-    if (!aligned16(X) || !aligned16(dY) || !aligned16(dW))
+    if (!aligned16(X) || !aligned16(dY) || !aligned16(dW) || !aligned16(workspace))
         return MOEGG_ESHAPE;
     {
         const int64_t S = (int64_t)num_tokens * topk;
@@ -249,6 +250,10 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
         if (!fits(x_rows, K) || !fits(S, N))
             return MOEGG_ESHAPE;
     }
+    const int64_t ws_need = moegg::dw_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K);
+    const bool use_ws = workspace != nullptr && ws_need > 0;
+    if (workspace != nullptr && (int64_t)workspace_bytes < ws_need)
+        return MOEGG_EWORKSPACE;
     int cus = 0;
     if (device_cus(&cus) != 0)
         return MOEGG_EHIP;
@@ -267,7 +272,17 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     p.K = K;
     p.flags = flags;
     p.topk_div = moegg::make_fastdiv((uint32_t)topk);
+    p.ws = use_ws ? static_cast<char *>(workspace) : nullptr;
+    p.split_rows = use_ws ? moegg::dw_split_rows(p.S, N, K) : 0;
     return from_hip(moegg::dw_launch(p, cus, static_cast<hipStream_t>(stream)));
+}
+
+size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
+                                             int32_t num_experts, int32_t N, int32_t K)
+{
+    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
+        return 0;
+    return (size_t)moegg::dw_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K);
 }
 
 moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_groups,

@@ -1393,48 +1393,101 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
     __shared__ int s_roff[kMaxExperts + 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_order[kMaxExperts];
+    __shared__ int s_crows[kMaxExperts];       // rows per chunk, by sorted position
+    __shared__ int s_istart[kMaxExperts + 1];  // first work item, by sorted position
+    __shared__ int s_poff[kMaxExperts + 1];    // first partial (split experts), by position
     __shared__ int s_dst[C::BM];
-    __shared__ int s_scratch[2];
+    __shared__ int s_scratch[4];
 
     const bool f32out = a.flags & MOEGG_DW_FP32_OUT;
     const int ntn = (a.N + C::BM - 1) / C::BM, ntk = (a.K + C::BN - 1) / C::BN;
     const int per_expert = ntn * ntk;
     build_expert_tables(a.m_sizes, a.E, a.S, s_roff, s_tstart, s_scratch, a.err,
                         [&](int) { return 0; });
-    // Longest experts first: the hot experts' long reductions start early.
+    // Chunks: an expert longer than split_rows is cut into c chunks of cr
+    // rows (a multiple of BK, the last one shorter); otherwise one chunk of
+    // all its rows.  Work items (chunk x output tile) are ordered by chunk
+    // length, longest first, so the long reductions start early.
+    auto chunking = [&](int m, int &c, int &cr) {
+        c = 1;
+        cr = m;
+        if (a.split_rows > 0 && m > a.split_rows) {
+            c = (m + a.split_rows - 1) / a.split_rows;
+            cr = ((m + c - 1) / c + BK - 1) / BK * BK;
+            c = (m + cr - 1) / cr;
+        }
+    };
+    int *const s_cnt = s_tstart;  // chunks by sorted position (s_tstart is free here)
     for (int e = threadIdx.x; e < a.E; e += C::NT) {
-        const int m = s_roff[e + 1] - s_roff[e];
+        int c, cr;
+        chunking(s_roff[e + 1] - s_roff[e], c, cr);
         int rank = 0;
         for (int f = 0; f < a.E; ++f) {
-            const int mf = s_roff[f + 1] - s_roff[f];
-            rank += (mf > m) || (mf == m && f < e);
+            int cf, crf;
+            chunking(s_roff[f + 1] - s_roff[f], cf, crf);
+            rank += (crf > cr) || (crf == cr && f < e);
         }
         s_order[rank] = e;
+        s_crows[rank] = cr;
+        s_cnt[rank] = c;
+        s_istart[rank] = c * per_expert;
+        s_poff[rank] = c > 1 ? c : 0;
     }
-    __syncthreads();
-    const int total = a.E * per_expert;
+    wave0_exclusive_scan(s_istart, a.E, &s_scratch[2]);
+    wave0_exclusive_scan(s_poff, a.E, &s_scratch[3]);
+    const int total = s_scratch[2];
+    float *const partials =
+        a.ws ? reinterpret_cast<float *>(a.ws + dw_header_bytes(a.E)) : nullptr;
+    if (blockIdx.x == 0 && a.split_rows > 0 && a.ws) {
+        // The plan for dw_reduce: split experts in sorted order.
+        int32_t *hdr = reinterpret_cast<int32_t *>(a.ws);
+        if (threadIdx.x < kWave) {
+            int base = 0;
+            for (int p0 = 0; p0 < a.E; p0 += kWave) {
+                const int pos = p0 + threadIdx.x;
+                const int cnt = pos < a.E ? s_cnt[pos] : 0;
+                const bool split = cnt > 1;
+                const uint64_t mask = __ballot(split);
+                const int j = base + __popcll(mask & ((1ull << threadIdx.x) - 1));
+                if (split) {
+                    hdr[1 + 3 * j] = s_order[pos];
+                    hdr[2 + 3 * j] = cnt;
+                    hdr[3 + 3 * j] = s_poff[pos];
+                }
+                base += __popcll(mask);
+            }
+            if (threadIdx.x == 0)
+                hdr[0] = base;
+        }
+    }
     const int64_t dy_row = (int64_t)a.N * 2, x_row = (int64_t)a.K * 2;
     const int64_t x_rows = PX ? a.S / a.topk : a.S;
     const u32x4_t dyr = rsrc_words(a.dY, a.S * dy_row);
     const u32x4_t xr = rsrc_words(a.X, x_rows * x_row);
 
     for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
-        const int e = __builtin_amdgcn_readfirstlane(s_order[t / per_expert]);
+        const int pos = __builtin_amdgcn_readfirstlane(upper_index(s_istart, a.E, t));
+        const int e = __builtin_amdgcn_readfirstlane(s_order[pos]);
+        const int item = t - __builtin_amdgcn_readfirstlane(s_istart[pos]);
+        const int chunk = item / per_expert;
+        const int cr = __builtin_amdgcn_readfirstlane(s_crows[pos]);
+        const int m_e = __builtin_amdgcn_readfirstlane(s_roff[e + 1] - s_roff[e]);
+        const bool split = cr < m_e;  // chunked expert: fp32 partial into the workspace
         // Grouped raster inside the expert: runs of up to kGroupK K-panels per
         // N column, so consecutive tiles (one XCD's concurrent set) share
         // few dY (N) and X (K) panels in that XCD's L2.
-        const int u = t % per_expert;
+        const int u = item % per_expert;
         const int span = kGroupK * ntn;
         const int first_kt = (u / span) * kGroupK;
         const int gk = min(ntk - first_kt, kGroupK);
         const int kt = first_kt + (u % span) % gk, nt = (u % span) / gk;
         const int n0 = nt * C::BM, k0 = kt * C::BN;
-        const int start = __builtin_amdgcn_readfirstlane(s_roff[e]);
-        const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1]) - start;
+        const int start = __builtin_amdgcn_readfirstlane(s_roff[e]) + chunk * cr;
+        const int mc = max(0, min(cr, m_e - chunk * cr));
 
         __syncthreads();
         for (int i = threadIdx.x; i < C::BM; i += C::NT)
-            s_dst[i] = (n0 + i < a.N) ? e * a.N + n0 + i : -1;
+            s_dst[i] = (n0 + i < a.N) ? (split ? 0 : e * a.N) + n0 + i : -1;
         __syncthreads();
 
         const int64_t S = a.S;
@@ -1533,10 +1586,51 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
                 },
             min(C::BM, a.N - n0));
         }
-        if (f32out)
+        if (split) {
+            const int poff = __builtin_amdgcn_readfirstlane(s_poff[pos]);
+            epilogue_f32<C>(acc, s_dst, partials + (int64_t)(poff + chunk) * a.N * a.K, a.K, k0,
+                            a.K);
+        } else if (f32out) {
             epilogue_f32<C>(acc, s_dst, reinterpret_cast<float *>(a.dW), a.K, k0, a.K);
-        else
+        } else {
             epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dW, a.K, k0, a.K);
+        }
+    }
+}
+
+// Sums the chunk partials of the split experts in chunk order (fp32) into
+// dW (bf16 or fp32), four elements per lane.  The plan comes from the
+// workspace header written by dw_kernel's block 0 earlier on the stream.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(DwParams a)
+{
+    const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws);
+    const float *partials = reinterpret_cast<const float *>(a.ws + dw_header_bytes(a.E));
+    const int nsplit = hdr[0];
+    const int64_t nk4 = (int64_t)a.N * a.K / 4;
+    const bool f32out = a.flags & MOEGG_DW_FP32_OUT;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsplit * nk4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int j = (int)(i / nk4);
+        const int64_t w = i - j * nk4;
+        const int e = hdr[1 + 3 * j], c = hdr[2 + 3 * j], p0 = hdr[3 + 3 * j];
+        float4 sum = reinterpret_cast<const float4 *>(partials + (int64_t)p0 * nk4 * 4)[w];
+        for (int q = 1; q < c; ++q) {
+            const float4 v =
+                reinterpret_cast<const float4 *>(partials + (int64_t)(p0 + q) * nk4 * 4)[w];
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+        }
+        const int64_t o = (int64_t)e * nk4 + w;
+        if (f32out) {
+            reinterpret_cast<float4 *>(a.dW)[o] = sum;
+        } else {
+            uint2 b;
+            b.x = pack_bf16x2(sum.x, sum.y);
+            b.y = pack_bf16x2(sum.z, sum.w);
+            reinterpret_cast<uint2 *>(a.dW)[o] = b;
+        }
     }
 }
 
@@ -1739,6 +1833,35 @@ hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Split reductions.  The target is about three work items per workgroup of
+// a full 256-CU chip when the rows are spread evenly over the experts:
+// chunks of S * tiles_per_expert / (256 * 3) rows (at least 4 reduction
+// steps), so that with the longest items scheduled first no workgroup is
+// left with one hot expert's whole reduction.  An expert splits only if it
+// has more rows than that; a split expert has fewer than 2 m / split_rows
+// chunks, so all of them together hold fewer than 2 S / split_rows partials.
+constexpr int kSplitCus = 256, kSplitItems = 3;
+
+int dw_split_rows(int64_t S, int N, int K)
+{
+    using C = DwCfg;
+    const int64_t tiles = (int64_t)((N + C::BM - 1) / C::BM) * ((K + C::BN - 1) / C::BN);
+    int64_t rows = (S * tiles + kSplitCus * kSplitItems - 1) / (kSplitCus * kSplitItems);
+    rows = (rows + BK - 1) / BK * BK;
+    if (rows < 4 * BK)
+        rows = 4 * BK;
+    return rows >= S ? 0 : (int)rows;
+}
+
+int64_t dw_workspace_bytes(int64_t S, int E, int N, int K)
+{
+    const int rows = dw_split_rows(S, N, K);
+    if (rows == 0)
+        return 0;
+    const int64_t partials = 2 * S / rows;
+    return dw_header_bytes(E) + partials * N * K * 4;
+}
+
 template <bool PX, bool PY>
 static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 {
@@ -1758,6 +1881,8 @@ hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
         dw_launch_flags<false, true>(p, cus, stream);
     else
         dw_launch_flags<false, false>(p, cus, stream);
+    if (p.split_rows > 0 && p.ws)
+        hipLaunchKernelGGL(dw_reduce_kernel, dim3(cus * 8), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -52,6 +52,13 @@ inline FastDiv make_fastdiv(uint32_t d)
 }
 
 // dW_e = dY_e^T X_e.
+//
+// Split reduction: with split_rows > 0, an expert with more than split_rows
+// rows has its reduction cut into chunks of about equal length (a multiple of
+// the reduction step); each chunk's tile writes an fp32 partial [N, K] into
+// the workspace and dw_reduce_launch sums the chunks in chunk order.  The
+// workspace starts with a header (int32: number of split experts, then
+// (expert, chunks, first partial) per split expert) of dw_header_bytes(E).
 struct DwParams {
     const char *X;
     const char *dY;
@@ -59,8 +66,10 @@ struct DwParams {
     const int32_t *gather;
     char *dW;
     int32_t *err;
+    char *ws;          // workspace (header + partials), or null
     int64_t S;
     int topk, E, N, K;
+    int split_rows;    // 0: never split
     uint32_t flags;
     FastDiv topk_div;
 };
@@ -99,6 +108,16 @@ struct CombineBwdParams {
 hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream);
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream);
 hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream);
+
+// Split plan sizes: rows per chunk for a launch of S rows (0: no expert can
+// split), the header size and the whole workspace (0 when no split is possible).
+int dw_split_rows(int64_t S, int N, int K);
+int64_t dw_workspace_bytes(int64_t S, int E, int N, int K);
+
+__host__ __device__ inline int64_t dw_header_bytes(int E)
+{
+    return (4 + 12 * (int64_t)E + 255) / 256 * 256;
+}
 hipError_t groups_launch(const GroupsParams &p, int trans_b, int cus, hipStream_t stream);
 
 hipError_t combine_launch(const CombineParams &p, hipStream_t stream);

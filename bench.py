@@ -110,7 +110,9 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
         dw_ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
         def bwd_dx():
-            mg.grouped_gemm_dX(dY, Ws[0], route_out["m_sizes"], route_out["gather"], topk,
+            # with rotated weights, not the copy the forward just read
+            W = Ws[(it["i"] - 1 + len(Ws) // 2) % len(Ws)]
+            mg.grouped_gemm_dX(dY, W, route_out["m_sizes"], route_out["gather"], topk,
                                bwd_flags, dX=dX)
 
         def bwd_dw():
@@ -187,6 +189,9 @@ def make_step(name):
         return build_layer_step(synth.fine_down(), dY_seed=0, with_bwd=False)
     if name == "decode":
         return build_layer_step(synth.fine_decode(), dY_seed=0, with_bwd=False, rotate=4)
+    if name == "decode_bwd":
+        return build_layer_step(synth.fine_decode_bwd(), dY_seed=synth.SEEDS["fine_bwd_dy"],
+                                rotate=4)
     if name == "tiny":
         return build_layer_step(synth.tiny(), dY_seed=0, with_bwd=False)
     if name == "dual":
@@ -206,6 +211,8 @@ WORKLOAD_DESC = {
             "step = route + fwd(permute_y+fuse_mul_post) + dX + dW",
     "fine_fwd": "fine-grained MoE down grouped GEMM forward, T=8192 E=128 top-8 K=768 N=2048",
     "decode": "fine-grained MoE down grouped GEMM decode slice, T=64 E=128 top-8 K=768 N=2048",
+    "decode_bwd": "decode-shaped backward of the fine-grained down GEMM, T=64 E=128 top-8 K=768 "
+                  "N=2048; step = route + fwd(permute_y) + dX + dW",
     "dual": "asymmetric dual-expert GEMM: [512,1024]x[1024,2048] and [256,1024]x[1024,4096]",
     "tiny": "tiny MoE grouped GEMM, T=128 K=256 N=512 E=8 top-2, permute_x",
     "combine": "top-k combine after the fine-grained down projection, T=8192 top-8 N=2048 "

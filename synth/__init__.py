@@ -176,6 +176,14 @@ def fine_bwd(**kw) -> Workload:
     return wl
 
 
+def fine_decode_bwd(T=64, K=768, N=2048, E=128, topk=8, s=1.2) -> Workload:
+    """The decode slice with an output gradient: the decode-shaped backward."""
+    wl = _fine("fine_decode_bwd", T, K, N, E, topk, s, SEEDS["fine_decode"], SEEDS["fine_down"],
+               True)
+    wl.flags = PERMUTE_Y
+    return wl
+
+
 def random_routing(T: int, E: int, topk: int, g: torch.Generator, empty=()):
     """Uniform random top-k routing (distinct experts per token) avoiding `empty` experts."""
     allowed = torch.tensor([e for e in range(E) if e not in set(empty)], dtype=torch.int64)
@@ -201,4 +209,4 @@ def random_case(T: int, K: int, N: int, E: int, topk: int, flags: int, seed: int
 
 
 BUILDERS = {"tiny": tiny, "dual": dual, "mixtral": mixtral, "fine_down": fine_down,
-            "fine_decode": fine_decode, "fine_bwd": fine_bwd}
+            "fine_decode": fine_decode, "fine_bwd": fine_bwd, "fine_decode_bwd": fine_decode_bwd}

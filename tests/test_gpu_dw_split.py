@@ -72,6 +72,7 @@ HOT = [
     # T, K, N, E, topk, seed -- tails in N and K, one expert far above split_rows
     (1200, 136, 264, 6, 2, 51),
     (900, 320, 520, 10, 3, 52),
+    (1024, 136, 264, 64, 2, 56),   # 32 rows per expert on average, many small experts
 ]
 
 

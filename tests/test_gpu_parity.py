@@ -244,7 +244,8 @@ def _bwd_case(mg, wl, flags, dw_flags_extra=0, rows_dx=None, rows_dw=None, cols_
 BWD_SMALL = [
     (300, 320, 264, 5, 2, 11, (3,)),
     (700, 136, 520, 6, 3, 12, (0,)),
-    (33, 64, 136, 40, 8, 13, (1, 5, 39)),
+    (33, 64, 136, 40, 8, 13, (1, 5, 39)),   # avg 6 rows/expert -> small-M dX tiles
+    (100, 200, 264, 24, 4, 15, (3,)),        # small-M dX tiles with K and N tails
 ]
 
 
@@ -292,6 +293,16 @@ def test_bwd_mixtral_sampled(mg):
                                          cols_dx=cols_dx, cols_dw=cols_dw)
     _assert_close(gdx, rdx, "dX mixtral sampled")
     _assert_close(gdw, rdw, "dW mixtral sampled")
+
+
+def test_bwd_decode_full(mg):
+    # the decode-shaped backward (T = 64 of the fine-grained layer), every output
+    wl = synth.fine_decode_bwd()
+    gdx, rdx, gdw, rdw, dW, ref_route = _bwd_case(mg, wl, wl.flags)
+    _assert_close(gdx, rdx, "dX decode")
+    _assert_close(gdw, rdw, "dW decode")
+    for e in np.nonzero(ref_route["m_sizes"] == 0)[0]:
+        assert torch.count_nonzero(dW[int(e)]).item() == 0
 
 
 def test_dw_fp32_out(mg):

@@ -702,21 +702,25 @@ struct UseQuad {
 //               a fragment is one 16-byte read.
 //   TR = true:  32 reduction rows of COLS elements (tr_off layout); a
 //               fragment is two transpose reads, rows r and r + 4 (tr_frag).
+// For TR the second step's rows are 16 below the first's with the same
+// swizzle (16 is a multiple of 4), so only step 0's offsets are kept and
+// step 1 adds a constant that folds into the read's immediate offset.
 template <bool TR, int COLS>
 struct OpFrag {
-    uint32_t off[2][4];
+    static constexpr int KK = TR ? 1 : 2;
+    uint32_t off[KK][4];
 
     // first: the wave's first row (TR = false) or column (TR = true).
     __device__ __forceinline__ void init(int first)
     {
         const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if constexpr (TR) {
                     const int q = lane & 15;
-                    const int row = kk * 16 + 8 * (lane >> 5) + (q >> 2);
+                    const int row = 8 * (lane >> 5) + (q >> 2);
                     const int col = first + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (q & 3);
                     off[kk][i] = (uint32_t)(tr_off<COLS>(row, col >> 3) + (col & 7) * 2);
                 } else {
@@ -730,10 +734,10 @@ struct OpFrag {
     {
         if constexpr (TR) {
             typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
-            const v4i16_t lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(part + off[kk][i]));
-            const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16 *)(part + off[kk][i] + 4 * COLS * 2));
+            const char *p = part + off[0][i] + kk * 16 * COLS * 2;
+            const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+            const v4i16_t hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 4 * COLS * 2));
             const v4i16_t both[2] = {lo, hi};
             return __builtin_bit_cast(bf16x8_t, both);
         } else {
@@ -1599,37 +1603,45 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
 }
 
 // Sums the chunk partials of the split experts in chunk order (fp32) into
-// dW (bf16 or fp32), four elements per lane.  The plan comes from the
-// workspace header written by dw_kernel's block 0 earlier on the stream.
+// dW (bf16 or fp32), 16 bytes per lane and two positions per iteration (so
+// that 2 c loads are in flight before the first add).  The plan comes from
+// the workspace header written by dw_kernel's workgroup 0 earlier on the
+// stream.
+__device__ __forceinline__ void dw_reduce_store(const DwParams &a, int64_t o, const float4 &v)
+{
+    if (a.flags & MOEGG_DW_FP32_OUT) {
+        reinterpret_cast<float4 *>(a.dW)[o] = v;
+    } else {
+        uint2 b;
+        b.x = pack_bf16x2(v.x, v.y);
+        b.y = pack_bf16x2(v.z, v.w);
+        reinterpret_cast<uint2 *>(a.dW)[o] = b;
+    }
+}
+
 __global__ __launch_bounds__(256) void dw_reduce_kernel(DwParams a)
 {
     const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws);
-    const float *partials = reinterpret_cast<const float *>(a.ws + dw_header_bytes(a.E));
+    const float4 *partials = reinterpret_cast<const float4 *>(a.ws + dw_header_bytes(a.E));
     const int nsplit = hdr[0];
     const int64_t nk4 = (int64_t)a.N * a.K / 4;
-    const bool f32out = a.flags & MOEGG_DW_FP32_OUT;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nsplit * nk4;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int j = (int)(i / nk4);
-        const int64_t w = i - j * nk4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int j = 0; j < nsplit; ++j) {
         const int e = hdr[1 + 3 * j], c = hdr[2 + 3 * j], p0 = hdr[3 + 3 * j];
-        float4 sum = reinterpret_cast<const float4 *>(partials + (int64_t)p0 * nk4 * 4)[w];
-        for (int q = 1; q < c; ++q) {
-            const float4 v =
-                reinterpret_cast<const float4 *>(partials + (int64_t)(p0 + q) * nk4 * 4)[w];
-            sum.x += v.x;
-            sum.y += v.y;
-            sum.z += v.z;
-            sum.w += v.w;
-        }
-        const int64_t o = (int64_t)e * nk4 + w;
-        if (f32out) {
-            reinterpret_cast<float4 *>(a.dW)[o] = sum;
-        } else {
-            uint2 b;
-            b.x = pack_bf16x2(sum.x, sum.y);
-            b.y = pack_bf16x2(sum.z, sum.w);
-            reinterpret_cast<uint2 *>(a.dW)[o] = b;
+        const float4 *src = partials + (int64_t)p0 * nk4;
+        for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nk4; w += 2 * stride) {
+            const bool two = w + stride < nk4;
+            float4 s0 = src[w];
+            float4 s1 = two ? src[w + stride] : float4{};
+            for (int q = 1; q < c; ++q) {
+                const float4 v0 = src[q * nk4 + w];
+                const float4 v1 = two ? src[q * nk4 + w + stride] : float4{};
+                s0.x += v0.x; s0.y += v0.y; s0.z += v0.z; s0.w += v0.w;
+                s1.x += v1.x; s1.y += v1.y; s1.z += v1.z; s1.w += v1.w;
+            }
+            dw_reduce_store(a, (int64_t)e * nk4 + w, s0);
+            if (two)
+                dw_reduce_store(a, (int64_t)e * nk4 + w + stride, s1);
         }
     }
 }
@@ -1745,6 +1757,7 @@ using DxCfg = Cfg<MOEGG_DX_CFG>;
 using DxQuadCfg = Cfg<256, 256, 2, 2>;  // long reductions: four-wave engine
 using DwCfg = Cfg<MOEGG_DW_CFG>;
 using SmallCfg = Cfg<MOEGG_SMALL_CFG>;   // few rows per expert: stream the weights
+using DxSmallCfg = Cfg<32, 128, 1, 4>;     // the same for dX
 using SmallGatedCfg = Cfg<32, 256, 1, 4>;  // the same with two blocks per wave to pair
 using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
 
@@ -1755,6 +1768,7 @@ template __global__ void fwd_kernel<BigCfg, true>(FwdParams);
 template __global__ void fwd_kernel<SmallGatedCfg, true>(FwdParams);
 template __global__ void dx_kernel<DxCfg>(DxParams);
 template __global__ void dx_kernel<DxQuadCfg>(DxParams);
+template __global__ void dx_kernel<DxSmallCfg>(DxParams);
 template __global__ void dw_kernel<DwCfg, false, false>(DwParams);
 template __global__ void dw_kernel<DwCfg, true, false>(DwParams);
 template __global__ void dw_kernel<DwCfg, false, true>(DwParams);
@@ -1824,9 +1838,19 @@ static void dx_launch_cfg(const DxParams &p, int cus, hipStream_t stream)
 // 2.16 ms against 2.44 ms); at N = 2048 the eight-wave engine is.
 constexpr int kDxQuadMinN = 8192;
 
+// Average rows per expert below which dX uses the small-M tiles: the
+// weights are then streamed once per 32-row tile (a decode slice), where
+// 256 x 256 tiles would leave about one long, latency-bound tile per CU
+// (T=64 top-8 of E=128, N=2048, K=768: 0.064 ms against 0.114 ms).
+#ifndef MOEGG_SMALL_ROWS
+#define MOEGG_SMALL_ROWS 96
+#endif
+
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 {
-    if (p.N >= kDxQuadMinN)
+    if (p.S / p.E < MOEGG_SMALL_ROWS)
+        dx_launch_cfg<DxSmallCfg>(p, cus, stream);
+    else if (p.N >= kDxQuadMinN)
         dx_launch_cfg<DxQuadCfg>(p, cus, stream);
     else
         dx_launch_cfg<DxCfg>(p, cus, stream);
@@ -1866,12 +1890,17 @@ template <bool PX, bool PY>
 static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 {
     using C = DwCfg;
-    const int64_t tiles =
-        (int64_t)p.E * ((p.N + C::BM - 1) / C::BM) * ((p.K + C::BN - 1) / C::BN);
+    // Work items: every (expert, output tile) plus the extra chunks of split
+    // experts, fewer than 2 S / split_rows in all.
+    const int64_t per_expert = (int64_t)((p.N + C::BM - 1) / C::BM) * ((p.K + C::BN - 1) / C::BN);
+    int64_t tiles = p.E * per_expert;
+    if (p.split_rows > 0)
+        tiles += 2 * p.S / p.split_rows * per_expert;
     static int res = resident_blocks(dw_kernel<C, PX, PY>, C::NT);
     hipLaunchKernelGGL((dw_kernel<C, PX, PY>), dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0,
                        stream, p);
 }
+
 
 hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
 {

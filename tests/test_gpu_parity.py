@@ -305,6 +305,29 @@ def test_bwd_decode_full(mg):
         assert torch.count_nonzero(dW[int(e)]).item() == 0
 
 
+EDGE_SHAPES = [
+    # T, K, N, E, topk, seed, empty -- the expert-table capacity (E = 1024, about
+    # one row per expert, most experts empty) and the smallest legal K and N
+    (700, 64, 64, 1024, 2, 16, ()),
+    (50, 8, 8, 3, 2, 17, ()),
+    (1, 8, 16, 4, 1, 18, ()),
+]
+
+
+@pytest.mark.parametrize("flags", [PX, PY], ids=["px", "py"])
+@pytest.mark.parametrize("case", EDGE_SHAPES, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in EDGE_SHAPES])
+def test_edge_shapes(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty, with_dy=True)
+    got, ref, _ = _fwd_case(mg, wl, flags)
+    _assert_close(got, ref, f"fwd {case} flags={flags}")
+    gdx, rdx, gdw, rdw, dW, ref_route = _bwd_case(mg, wl, flags)
+    _assert_close(gdx, rdx, f"dX {case} flags={flags}")
+    _assert_close(gdw, rdw, f"dW {case} flags={flags}")
+    for e in np.nonzero(ref_route["m_sizes"] == 0)[0][:64]:
+        assert torch.count_nonzero(dW[int(e)]).item() == 0
+
+
 def test_dw_fp32_out(mg):
     wl = synth.random_case(300, 136, 264, 5, 2, PY, 21, empty=(2,), with_dy=True)
     _, _, gdw, rdw, dW, _ = _bwd_case(mg, wl, PY, dw_flags_extra=mg.DW_FP32_OUT)

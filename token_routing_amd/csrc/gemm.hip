@@ -1864,7 +1864,10 @@ hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 // left with one hot expert's whole reduction.  An expert splits only if it
 // has more rows than that; a split expert has fewer than 2 m / split_rows
 // chunks, so all of them together hold fewer than 2 S / split_rows partials.
-constexpr int kSplitCus = 256, kSplitItems = 3;
+#ifndef MOEGG_DW_SPLIT_ITEMS
+#define MOEGG_DW_SPLIT_ITEMS 3
+#endif
+constexpr int kSplitCus = 256, kSplitItems = MOEGG_DW_SPLIT_ITEMS;
 
 int dw_split_rows(int64_t S, int N, int K)
 {

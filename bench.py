@@ -390,6 +390,46 @@ def _counter_means(path, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
+MI355X_XCDS, MI355X_SIMDS = 8, 256 * 4
+
+
+def counter_lines(sq_dir, stat_rows):
+    """Per-kernel MFMA utilisation and LDS bank conflicts from an SQ counter
+    pass (SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT,
+    GRBM_GUI_ACTIVE), all from the same run.
+
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so a kernel's busy cycles are
+    GRBM_GUI_ACTIVE / 8; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over those
+    cycles x 1024 SIMDs.  The cycle count divided by the kernel's average
+    duration in the trace run (a different run, so only indicative) gives
+    the clock."""
+    import glob
+    f = glob.glob(os.path.join(sq_dir, "*counter_collection.csv"))[0]
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+             "GRBM_GUI_ACTIVE")
+    means = {n: _counter_means(f, n) for n in names}
+    dur = {}
+    for r in stat_rows:
+        lab = _label(r["Name"])
+        if lab and lab not in dur:
+            dur[lab] = float(r["AverageNs"])
+    out = ["", "Counters (their own pass; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+           "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = GRBM_GUI_ACTIVE / 8 / the trace "
+           "run's average duration, indicative only since the runs differ):", "",
+           "| kernel | MFMA busy | LDS bank conflicts / LDS active | clock GHz (indicative) |",
+           "|---|---|---|---|"]
+    for lab in ("fwd", "dX", "dW", "groups", "combine", "combine_bwd"):
+        g = means["GRBM_GUI_ACTIVE"].get(lab)
+        if not g or lab not in dur:
+            continue
+        cyc = g / MI355X_XCDS
+        busy = means["SQ_VALU_MFMA_BUSY_CYCLES"].get(lab, 0.0) / (cyc * MI355X_SIMDS)
+        act = means["SQ_LDS_IDX_ACTIVE"].get(lab, 0.0)
+        conf = means["SQ_LDS_BANK_CONFLICT"].get(lab, 0.0) / act if act else 0.0
+        out.append(f"| {lab} | {100 * busy:.1f}% | {conf:.4f} | {cyc / dur[lab]:.2f} |")
+    return out
+
+
 def summarize(prof_dir, workload, command):
     """Turn rocprofv3 CSV output under prof_dir (trace/, fetch/, write/,
     copy_FETCH_SIZE/, copy_WRITE_SIZE/) into profiles/ summaries: the kernel
@@ -435,6 +475,9 @@ def summarize(prof_dir, workload, command):
                        "write_scale": cal["WRITE_SIZE"]},
                       open(os.path.join(ROOT, "profiles", f"traffic_{lab}_{workload}.json"), "w"),
                       indent=1)
+    sq_dir = os.path.join(prof_dir, "sq")
+    if os.path.isdir(sq_dir):
+        lines += counter_lines(sq_dir, rows)
     out = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)

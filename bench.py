@@ -109,11 +109,14 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
         ws_bytes = mg.dw_workspace_bytes(T, topk, E, N, K)
         dw_ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
+        dx_bytes = mg.dx_workspace_bytes(T, topk, E, N, K)
+        dx_ws = torch.empty(dx_bytes, dtype=torch.uint8, device="cuda") if dx_bytes else None
+
         def bwd_dx():
             # with rotated weights, not the copy the forward just read
             W = Ws[(it["i"] - 1 + len(Ws) // 2) % len(Ws)]
             mg.grouped_gemm_dX(dY, W, route_out["m_sizes"], route_out["gather"], topk,
-                               bwd_flags, dX=dX)
+                               bwd_flags, dX=dX, workspace=dx_ws, split=dx_ws is not None)
 
         def bwd_dw():
             mg.grouped_gemm_dW(X, dY, route_out["m_sizes"], route_out["gather"], topk, bwd_flags,
@@ -363,7 +366,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
                  ("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
-                 ("dw_reduce_kernel", "dW_reduce"),
+                 ("dw_reduce_kernel", "dW_reduce"), ("tail_reduce_kernel", "tail_reduce"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),
                  ("route_scan", "route_scan"), ("route_scatter", "route_scatter"))
 

@@ -168,14 +168,36 @@ moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t 
  *   stored bf16 to row gather_idx[p] if the forward used PERMUTE_X (scatter
  *   back to slot order), else row p.  dY is [S, N], dX is [S, K]; summing a
  *   token's top-k rows is left to the caller.
+ *
+ * Tail balancing (optional): a persistent launch runs its tiles in rounds
+ * of one tile per workgroup.  With a workspace, the tiles of a last, partial
+ * round have their reductions over N cut into parts spread over the
+ * otherwise idle workgroups (the split-k of triton_kernels/matmul_ogs.py,
+ * fp32 partials summed by a separate launch), summed in part order:
+ * deterministic, and equal to the unsplit result up to fp32 rounding order.
+ *   workspace       device, 16-byte aligned, at least
+ *                   moegg_grouped_gemm_dX_workspace_bytes(...) bytes (no
+ *                   initialisation needed), or NULL: no split.
+ *   workspace_bytes its size; 0 with NULL.
  * Errors: EINVAL for both permute flags or a missing gather_idx;
  * EUNSUPPORTED for FUSE_MUL_POST (the pages forbid it in training);
- * ESHAPE as for the forward.
+ * ESHAPE as for the forward; EWORKSPACE for a workspace smaller than needed.
  */
 moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t *m_sizes,
                                    const int32_t *gather_idx, int32_t num_tokens, int32_t topk,
                                    int32_t num_experts, int32_t N, int32_t K, uint32_t flags,
-                                   void *dX, int32_t *error_flags, void *stream);
+                                   void *dX, void *workspace, size_t workspace_bytes,
+                                   int32_t *error_flags, void *stream);
+
+/*
+ * Bytes of workspace moegg_grouped_gemm_dX can use to balance its last
+ * round of tiles, for these sizes on the current device (it depends on the
+ * device's compute units): a small header plus fp32 partials of at most one
+ * tile per workgroup of the launch.  0 if the sizes are invalid or the
+ * device cannot be queried.
+ */
+size_t moegg_grouped_gemm_dX_workspace_bytes(int32_t num_tokens, int32_t topk,
+                                             int32_t num_experts, int32_t N, int32_t K);
 
 /*
  * moegg_grouped_gemm_dW -- dW_e = dY_e^T X_e, a reduction over each expert's

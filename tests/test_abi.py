@@ -88,10 +88,16 @@ def test_gated_shape_and_backward_checks(lib):
     assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 40, 64, GS | PX,
                                       FAKE, None, None) == ESHAPE
     # the backward kernels take no activation flag
-    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None,
-                                     None) == EINVAL
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None, 0,
+                                     None, None) == EINVAL
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None,
                                      0, None, None) == EINVAL
+
+
+def test_dx_workspace_checks(lib):
+    # invalid sizes answer 0 before the device is queried
+    assert lib.moegg_grouped_gemm_dX_workspace_bytes(-1, 2, 8, 64, 64) == 0
+    assert lib.moegg_grouped_gemm_dX_workspace_bytes(10, 2, 8, 60, 64) == 0
 
 
 def test_dw_workspace(lib):
@@ -115,16 +121,16 @@ def test_operand_size_limit(lib):
 
 
 def test_backward_rejects_fuse_mul(lib):
-    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None,
-                                     None) == EUNSUP
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None, 0,
+                                     None, None) == EUNSUP
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, FM, FAKE, None,
                                      0, None, None) == EUNSUP
     assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, PX | PY, FAKE,
-                                     None, None) == EINVAL
+                                     None, 0, None, None) == EINVAL
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, None, 10, 2, 8, 64, 64, PY, FAKE, None,
                                      0, None, None) == EINVAL
-    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, F32, FAKE, None,
-                                     None) == EINVAL
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, F32, FAKE, None, 0,
+                                     None, None) == EINVAL
 
 
 def test_route_checks(lib):

@@ -72,8 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moegg_grouped_gemm_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp,
                                            vp, vp]
     lib.moegg_grouped_gemm_fwd.restype = ctypes.c_int
-    lib.moegg_grouped_gemm_dX.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp, vp, vp]
+    lib.moegg_grouped_gemm_dX.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp, vp,
+                                          sz, vp, vp]
     lib.moegg_grouped_gemm_dX.restype = ctypes.c_int
+    lib.moegg_grouped_gemm_dX_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.moegg_grouped_gemm_dX_workspace_bytes.restype = sz
     lib.moegg_grouped_gemm_dW.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp, vp,
                                           sz, vp, vp]
     lib.moegg_grouped_gemm_dW.restype = ctypes.c_int
@@ -179,23 +182,43 @@ def grouped_gemm_fwd(X, W, m_sizes, gather_idx, topk_weights, topk: int, flags: 
         _stream(stream)), "moegg_grouped_gemm_fwd")
     return Y
 
+def dx_workspace_bytes(num_tokens: int, topk: int, num_experts: int, N: int, K: int) -> int:
+    """Workspace bytes that let grouped_gemm_dX balance its last round (current device)."""
+    return int(load_library().moegg_grouped_gemm_dX_workspace_bytes(num_tokens, topk,
+                                                                       num_experts, N, K))
+
+
+def _workspace(need: int, workspace, device):
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, 0
+    workspace = _device_tensor(workspace, torch.uint8, "workspace")
+    return workspace, workspace.numel()
+
 
 def grouped_gemm_dX(dY, W, m_sizes, gather_idx, topk: int, flags: int, *, dX=None,
-                    error_flags=None, stream=None):
-    """dX = grouped dY_e W_e; flags are the forward's permute flags. Returns bf16 [S, K]."""
+                    workspace=None, split: bool = True, error_flags=None, stream=None):
+    """dX = grouped dY_e W_e; flags are the forward's permute flags. Returns bf16 [S, K].
+
+    split: let the library balance the last round of tiles (fp32 partials in
+    `workspace`, a uint8 CUDA tensor of dx_workspace_bytes(...) bytes,
+    allocated here when not given).  split=False passes no workspace.
+    """
     lib = load_library()
     E, N, K = W.shape
     S = dY.shape[0]
     if dX is None:
         dX = torch.empty(S, K, dtype=torch.bfloat16, device=dY.device)
+    need = dx_workspace_bytes(S // topk, topk, E, N, K) if split else 0
+    ws, ws_bytes = _workspace(need, workspace if split else None, dY.device)
     _check(lib.moegg_grouped_gemm_dX(
         _ptr(_device_tensor(dY, torch.bfloat16, "dY")), _ptr(_device_tensor(W, torch.bfloat16, "W")),
         _ptr(_device_tensor(m_sizes, torch.int32, "m_sizes")),
         _ptr(_device_tensor(gather_idx, torch.int32, "gather_idx")), S // topk, topk, E, N, K,
-        int(flags), _ptr(_device_tensor(dX, torch.bfloat16, "dX")), _ptr(error_flags),
-        _stream(stream)), "moegg_grouped_gemm_dX")
+        int(flags), _ptr(_device_tensor(dX, torch.bfloat16, "dX")), _ptr(ws), ws_bytes,
+        _ptr(error_flags), _stream(stream)), "moegg_grouped_gemm_dX")
     return dX
-
 
 def dw_workspace_bytes(num_tokens: int, topk: int, num_experts: int, N: int, K: int) -> int:
     """Workspace bytes that let grouped_gemm_dW split hot experts' reductions (0: none)."""

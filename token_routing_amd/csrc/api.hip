@@ -185,7 +185,8 @@ moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t 
 moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t *m_sizes,
                                    const int32_t *gather_idx, int32_t num_tokens, int32_t topk,
                                    int32_t num_experts, int32_t N, int32_t K, uint32_t flags,
-                                   void *dX, int32_t *error_flags, void *stream)
+                                   void *dX, void *workspace, size_t workspace_bytes,
+                                   int32_t *error_flags, void *stream)
 {
     moegg_status st = check_gemm_common(num_tokens, topk, num_experts, N, K);
     if (st != MOEGG_OK)
@@ -200,14 +201,19 @@ moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t 
         return MOEGG_OK;
     if (dY == nullptr || W == nullptr || m_sizes == nullptr || dX == nullptr)
         return MOEGG_EINVAL;
-    if (!aligned16(dY) || !aligned16(W) || !aligned16(dX))
+    if (!aligned16(dY) || !aligned16(W) || !aligned16(dX) || !aligned16(workspace))
         return MOEGG_ESHAPE;
     if (!fits((int64_t)num_tokens * topk, N) || !fits(N, K))
         return MOEGG_ESHAPE;
     int cus = 0;
     if (device_cus(&cus) != 0)
         return MOEGG_EHIP;
+    const int64_t ws_need =
+        moegg::dx_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K, cus);
+    if (workspace != nullptr && (int64_t)workspace_bytes < ws_need)
+        return MOEGG_EWORKSPACE;
     moegg::DxParams p;
+    p.ws = workspace != nullptr && ws_need > 0 ? static_cast<char *>(workspace) : nullptr;
     p.dY = static_cast<const char *>(dY);
     p.W = static_cast<const char *>(W);
     p.m_sizes = m_sizes;
@@ -275,6 +281,17 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     p.ws = use_ws ? static_cast<char *>(workspace) : nullptr;
     p.split_rows = use_ws ? moegg::dw_split_rows(p.S, N, K) : 0;
     return from_hip(moegg::dw_launch(p, cus, static_cast<hipStream_t>(stream)));
+}
+
+size_t moegg_grouped_gemm_dX_workspace_bytes(int32_t num_tokens, int32_t topk,
+                                             int32_t num_experts, int32_t N, int32_t K)
+{
+    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
+        return 0;
+    int cus = 0;
+    if (device_cus(&cus) != 0)
+        return 0;
+    return (size_t)moegg::dx_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K, cus);
 }
 
 size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,

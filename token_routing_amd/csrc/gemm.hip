@@ -1,31 +1,32 @@
 // Persistent grouped-GEMM kernels for gfx950: forward (with permute_x,
-// permute_y and fuse_mul_post), dX, dW (ragged reduction per expert) and
-// explicit GEMM groups.
+// permute_y, fuse_mul_post and the gated activation), dX, dW (ragged
+// reduction per expert, optionally split for hot experts) and explicit GEMM
+// groups.
 //
 // The operations are those of grouped_gemm_forward / grouped_gemm_dX /
 // grouped_gemm_dW (unsloth grouped_gemm/interface.py), whose per-expert
 // meaning is the loop of matmul_ogs_torch (triton_kernels/matmul_ogs.py), and
 // of asym_dual_gmm_separated (wall_x/fusions/backend.py) for the groups.
 //
-// One engine serves all four.  A workgroup owns an output tile of BM x BN and
-// walks the reduction in stages of BK = 64 elements:
-//   * LDS holds both operands "reduction-contiguous": a tile row is the 64
-//     reduction elements (128 bytes) of one output row (A) or output column
-//     (B).  16-byte chunk c of row r lives at chunk c ^ (r & 7), so the eight
-//     lanes that read one chunk column of eight consecutive rows hit eight
-//     different bank groups.
-//   * v_mfma_f32_32x32x16_bf16 consumes the tile: lane l reads 8 reduction
-//     elements of row (l % 32) for A and of column (l % 32) for B.
+// One engine serves all of them.  A workgroup owns an output tile of BM x BN
+// and walks the reduction in stages of BK = 64 elements:
 //   * Operands whose reduction index is contiguous in HBM (X and W in the
-//     forward, dY in dX) are copied 16 bytes per lane, eight lanes per
-//     128-byte row segment; gathered rows (permute_x, permute_y on load) are
-//     just per-row base pointers.
+//     forward, dY in dX) sit in LDS "reduction-contiguous": a tile row is the
+//     64 reduction elements (128 bytes) of one output row or column, 16-byte
+//     chunk c of row r at chunk c ^ ((r / 2) mod 8), so 16 rows read at one
+//     chunk hit 16 different bank groups.
 //   * Operands whose reduction index runs across HBM rows (W in dX, dY and X
-//     in dW, a [K, N] weight in the groups) are read as 8 x 8 element blocks
-//     (eight 16-byte row segments), transposed in registers and written as
-//     eight 16-byte LDS chunks.
-//   * Two LDS stages: global loads for stage s+1 are in flight while the
-//     MFMAs consume stage s; one barrier per stage.
+//     in dW, a [K, N] weight in the groups) sit in LDS as in HBM (reduction
+//     rows), chunks swizzled by (row mod 4) * 4, and their MFMA fragments are
+//     read with the transposing LDS read ds_read_b64_tr_b16.
+//   * Both are copied HBM -> LDS by buffer_load ... lds (no registers), 16
+//     bytes per lane, whole 128-byte row segments per eight lanes; gathered
+//     rows (permute_x, permute_y on load) are just per-lane row offsets.
+//   * v_mfma_f32_32x32x16_bf16 with fp32 accumulators; fragment reads run one
+//     16-deep step ahead of the MFMAs.  Two LDS stages: the copies of stage
+//     s+1 are in flight while the MFMAs consume stage s; one barrier per
+//     stage.  Long dX reductions use a four-wave engine with four 32-deep
+//     slots instead (see below).
 //   * bf16 epilogue: fp32 accumulators (times the gate weight under
 //     fuse_mul_post) are rounded to bf16 into LDS, then written out as
 //     16-byte row segments, to row gather[p] under permute_y.
@@ -322,7 +323,7 @@ struct TileDmaLoader {
 
     // Turn the raw indices fetched last into byte offsets: fin(red, raw) ->
     // HBM row (-1: zeros); row_bytes is the HBM pitch.  Call before issuing
-    // any copy of the stage (see mainloop_load below).
+    // any copy of the stage (the load callbacks of dx_kernel and dw_kernel).
     template <class FinFn>
     __device__ __forceinline__ void prepare(int col0, int ncols, int64_t row_bytes, FinFn fin)
     {
@@ -472,10 +473,10 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
                 acc[i][j][r] = 0.0f;
 }
 
-// Direct operands are copied HBM -> LDS by DmaLoader (ASYNC) or staged
-// through registers by DirectLoader.  Measured on MI355X: the copies are
-// faster in the forward (both operands direct); in dX, whose other operand is
-// register-staged, register staging of both is faster.
+// Every operand is copied HBM -> LDS without passing through registers
+// (DmaLoader, TileDmaLoader).  Setting one of these switches to 0 builds the
+// register-staged loader (DirectLoader, RowTileLoader) instead, for
+// comparison; on MI355X the copies measured faster wherever they are used.
 #ifndef MOEGG_FWD_DMA
 #define MOEGG_FWD_DMA 1
 #endif
@@ -1166,6 +1167,90 @@ __device__ __forceinline__ int checked_gather(const int32_t *gather, int64_t p, 
 }
 
 // ---------------------------------------------------------------------------
+// Tail split of the last round (dX; see TailReduceParams in gemm_params.h).
+// Measured on the Mixtral shape in one process: dX 2.03 -> 1.90 ms.  The same
+// split of the forward (K reduction, the gate factor and scatter applied after
+// the sum) measured slower (1.75 -> 1.81 ms) and is not used.
+// ---------------------------------------------------------------------------
+
+struct TailPlan {
+    int full;   // work items 0 .. full-1 are whole tiles
+    int R, P;   // tail tiles after them, parts per tail tile (R = 0: none)
+    int items;  // full + R * P
+};
+
+// The same plan in every workgroup (total and G are uniform).  Splitting pays
+// when at least two workgroups share each tail tile.
+__device__ __forceinline__ TailPlan tail_plan(int total, int G, bool enabled)
+{
+    TailPlan tp{total, 0, 1, total};
+    if (enabled && G <= kTailMaxTiles) {
+        const int R = total % G;
+        if (R > 0 && G / R >= 2) {
+            tp.full = total - R;
+            tp.R = R;
+            tp.P = G / R;
+            tp.items = tp.full + R * tp.P;
+        }
+    }
+    return tp;
+}
+
+// Work item w -> tile and part (part -1: a whole tile).
+__device__ __forceinline__ void tail_item(const TailPlan &tp, int w, int &t, int &part)
+{
+    if (w < tp.full) {
+        t = w;
+        part = -1;
+    } else {
+        t = tp.full + (w - tp.full) / tp.P;
+        part = (w - tp.full) % tp.P;
+    }
+}
+
+// Sums each tail tile's parts in part order and stores it (bf16, 8 bytes per
+// lane), after the GEMM launch on the same stream.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduceParams a)
+{
+    const int32_t *hdr = reinterpret_cast<const int32_t *>(a.ws);
+    const float4 *partials = reinterpret_cast<const float4 *>(a.ws + tail_header_bytes());
+    const int R = hdr[0], P = hdr[1];
+    constexpr int Q = BN / 4;  // float4 per tile row
+    for (int r = 0; r < R; ++r) {
+        const int p0 = hdr[2 + 4 * r], rows = hdr[3 + 4 * r], c0 = hdr[4 + 4 * r];
+        for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < rows * Q;
+             idx += gridDim.x * blockDim.x) {
+            const int i = idx / Q, j = idx % Q;
+            const int col = c0 + 4 * j;
+            if (col >= a.ncols)
+                continue;
+            const int64_t p = p0 + i;
+            int64_t dst = p;
+            if (a.scatter_out) {
+                const int g = a.gather[p];
+                if (g < 0 || g >= a.S)
+                    continue;  // reported by the GEMM launch
+                dst = g;
+            }
+            const float4 *src = partials + (int64_t)r * P * BM * Q + i * Q + j;
+            float4 s = src[0];
+            for (int q = 1; q < P; ++q) {
+                const float4 v = src[(int64_t)q * BM * Q];
+                s.x += v.x;
+                s.y += v.y;
+                s.z += v.z;
+                s.w += v.w;
+            }
+            uint2 b;
+            b.x = pack_bf16x2(s.x, s.y);
+            b.y = pack_bf16x2(s.z, s.w);
+            *reinterpret_cast<uint2 *>(a.out + (dst * a.ldo + col) * 2) = b;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
 
@@ -1280,8 +1365,16 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
     const int nsteps = (a.N + BK - 1) / BK;
     const int64_t dy_row = (int64_t)a.N * 2, w_row = (int64_t)a.K * 2;
     const u32x4_t dyr = rsrc_words(a.dY, a.S * dy_row);
+    const TailPlan tp = tail_plan(total, gridDim.x, a.ws != nullptr);
+    int32_t *const hdr = reinterpret_cast<int32_t *>(a.ws);
+    if (a.ws && blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[0] = tp.R;
+        hdr[1] = tp.P;
+    }
 
-    for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
+    for (int w = xcd_logical_block(blockIdx.x, gridDim.x); w < tp.items; w += gridDim.x) {
+        int t, part;
+        tail_item(tp, w, t, part);
         const int e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
         const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1] - s_roff[e]);
         const int p0base = __builtin_amdgcn_readfirstlane(s_roff[e]);
@@ -1291,6 +1384,16 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         const int p0 = p0base + mt * C::BM;
         const int rows = min(C::BM, mc - mt * C::BM);
         const int k0 = kt * C::BN;
+        // A tail part reduces its share of the N range into a partial whose
+        // row i is tile row i (the finishing launch maps rows to dX).
+        const bool tail = part >= 0;
+        const int r = t - tp.full;
+        if (tail && part == 0 && threadIdx.x == 0) {
+            hdr[2 + 4 * r] = p0;
+            hdr[3 + 4 * r] = rows;
+            hdr[4 + 4 * r] = k0;
+            hdr[5 + 4 * r] = e;
+        }
 
         for (int i = threadIdx.x; i < C::BM; i += C::NT) {
             int src = -1, dst = -1;
@@ -1303,9 +1406,13 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                 }
             }
             s_src[i] = src;
-            s_dst[i] = dst;
+            s_dst[i] = tail ? i : dst;
         }
         __syncthreads();
+        float *const partial =
+            tail ? reinterpret_cast<float *>(a.ws + tail_header_bytes()) +
+                       (int64_t)(r * tp.P + part) * C::BM * C::BN
+                 : nullptr;
 
         const u32x4_t wr =
             rsrc_words(a.W + (int64_t)e * a.N * w_row, (int64_t)a.N * w_row);
@@ -1323,17 +1430,25 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                 ca.set_row(j, s_src[ca.row(first, j)], dy_row);
             cb.init(smem + Q::A, 0, k0, a.K, w_row);
             const int N = a.N;
+            const int U = (N + SK - 1) / SK;
+            const int u0 = tail ? part * U / tp.P : 0, u1 = tail ? (part + 1) * U / tp.P : U;
             zero_acc<C>(acc);
             mainloop_quad<C, false, true>(
-                smem, (N + SK - 1) / SK, acc,
+                smem, u1 - u0, acc,
                 plain_copy([&](int q, int buf, int n) {
+                    const int qq = q + u0;
                     if (n < Q::NCA)
-                        ca.template issue_one<Q::SLOT>(dyr, n, buf, q * SK, N);
+                        ca.template issue_one<Q::SLOT>(dyr, n, buf, qq * SK, N);
                     else
-                        cb.template issue_one<Q::SLOT>(wr, n - Q::NCA, buf, q, N);
+                        cb.template issue_one<Q::SLOT>(wr, n - Q::NCA, buf, qq, N);
                 }),
                 rows);
-            epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+            if (tail) {
+                epilogue_f32<C>(acc, s_dst, partial, C::BN, 0, C::BN);
+                __syncthreads();
+            } else {
+                epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+            }
             continue;
         }
         RowLoader<C::BM, C::NT, MOEGG_DX_DMA != 0> la;
@@ -1341,20 +1456,22 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], dy_row);
         const int N = a.N;
+        const int u0 = tail ? part * nsteps / tp.P : 0;
+        const int u1 = tail ? (part + 1) * nsteps / tp.P : nsteps;
         zero_acc<C>(acc);
         if constexpr (MOEGG_TILE_DMA != 0) {
             TileDmaLoader<C::BN, C::NT> lb;
             auto wraw = [](int n) -> int { return n; };
             auto wfin = [=](int n, int) -> int { return n < N ? n : -1; };
-            lb.fetch(0, wraw);
+            lb.fetch(u0 * BK, wraw);
             mainloop<C, true, false, true>(
-                st0, st1, nsteps, acc,
+                st0, st1, u1 - u0, acc,
                 [&](int s, char *As, char *Bs) {
                     lb.prepare(k0, a.K, w_row, wfin);
                     __builtin_amdgcn_sched_barrier(0);
-                    la.load(dyr, As, s * BK, a.N);
+                    la.load(dyr, As, (s + u0) * BK, a.N);
                     lb.issue(wr, Bs);
-                    lb.fetch((s + 1) * BK, wraw);
+                    lb.fetch((s + u0 + 1) * BK, wraw);
                 },
                 [&](char *As, char *Bs) {
                     la.store(As);
@@ -1365,10 +1482,10 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
             RowTileLoader<C::BN, C::NT> lb;
             auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
             mainloop<C, true, false, true>(
-                st0, st1, nsteps, acc,
+                st0, st1, u1 - u0, acc,
                 [&](int s, char *As, char *) {
-                    la.load(dyr, As, s * BK, a.N);
-                    lb.load(wr, s * BK, k0, a.K, wrowfn);
+                    la.load(dyr, As, (s + u0) * BK, a.N);
+                    lb.load(wr, (s + u0) * BK, k0, a.K, wrowfn);
                 },
                 [&](char *As, char *Bs) {
                     la.store(As);
@@ -1376,7 +1493,12 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
                 },
             rows);
         }
-        epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+        if (tail) {
+            epilogue_f32<C>(acc, s_dst, partial, C::BN, 0, C::BN);
+            __syncthreads();
+        } else {
+            epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, a.dX, a.K, k0, a.K);
+        }
     }
 }
 
@@ -1826,11 +1948,30 @@ hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream)
 }
 
 template <class C>
+static int dx_resident()
+{
+    static int res = resident_blocks(dx_kernel<C>, C::NT);
+    return res;
+}
+
+template <class C>
 static void dx_launch_cfg(const DxParams &p, int cus, hipStream_t stream)
 {
     const int64_t tiles = n_blocks_bound(p.S, p.E, C::BM) * ((p.K + C::BN - 1) / C::BN);
-    static int res = resident_blocks(dx_kernel<C>, C::NT);
-    hipLaunchKernelGGL(dx_kernel<C>, dim3(grid_for(tiles, cus, res)), dim3(C::NT), 0, stream, p);
+    hipLaunchKernelGGL(dx_kernel<C>, dim3(grid_for(tiles, cus, dx_resident<C>())), dim3(C::NT), 0,
+                       stream, p);
+    if (p.ws) {
+        TailReduceParams r;
+        r.ws = p.ws;
+        r.out = p.dX;
+        r.gather = p.gather;
+        r.S = p.S;
+        r.ldo = p.K;
+        r.ncols = p.K;
+        r.scatter_out = p.flags & MOEGG_PERMUTE_X;
+        hipLaunchKernelGGL((tail_reduce_kernel<C::BM, C::BN>), dim3(cus * 4), dim3(256), 0, stream,
+                           r);
+    }
 }
 
 // Measured on MI355X: the four-wave engine is faster once the reduction (N)
@@ -1845,6 +1986,27 @@ constexpr int kDxQuadMinN = 8192;
 #ifndef MOEGG_SMALL_ROWS
 #define MOEGG_SMALL_ROWS 96
 #endif
+
+// Workspace of the tail split: the header and at most G partials of one
+// tile (R * P <= G), for the grid the launch below will use.
+template <class C>
+static int64_t dx_ws_cfg(int cus)
+{
+    const int64_t G = (int64_t)cus * dx_resident<C>();
+    return G > kTailMaxTiles ? 0 : tail_header_bytes() + G * C::BM * C::BN * 4;
+}
+
+// The small-M tiles are many and short (a decode slice): their last round
+// costs little, and the finishing launch would cost more.
+int64_t dx_workspace_bytes(int64_t S, int E, int N, int K, int cus)
+{
+    (void)K;
+    if (S / E < MOEGG_SMALL_ROWS)
+        return 0;
+    if (N >= kDxQuadMinN)
+        return dx_ws_cfg<DxQuadCfg>(cus);
+    return dx_ws_cfg<DxCfg>(cus);
+}
 
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 {

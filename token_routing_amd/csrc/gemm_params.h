@@ -22,7 +22,7 @@ struct FwdParams {
     uint32_t flags;
 };
 
-// dX = grouped dY_e W_e.
+// dX = grouped dY_e W_e.  ws: workspace for the tail split, or null.
 struct DxParams {
     const char *dY;
     const char *W;
@@ -30,9 +30,35 @@ struct DxParams {
     const int32_t *gather;
     char *dX;
     int32_t *err;
+    char *ws;
     int64_t S;
     int topk, E, N, K;
     uint32_t flags;
+};
+
+// Tail split (stream-K for the last round of a persistent grid): when the
+// tiles do not fill whole rounds of the G workgroups, each of the R tiles of
+// the last round has its reduction cut into P = G / R parts, one per
+// otherwise idle workgroup.  A part writes its fp32 [BM, BN] partial into the
+// workspace; a second launch sums the parts of each tile in part order and
+// stores the tile.  The workspace holds a header (int32: R, P, then p0, rows,
+// column 0 and expert of each tail tile; kTailMaxTiles entries) and then the
+// partials, tail tile r part q at index r * P + q.
+constexpr int kTailMaxTiles = 4096;
+__host__ __device__ inline int64_t tail_header_bytes()
+{
+    return ((2 + 4 * (int64_t)kTailMaxTiles) * 4 + 255) / 256 * 256;
+}
+
+// The finishing launch: out[dst(p0 + i), c0 + j] = sum_q partial[r * P +
+// q][i, j] as bf16, dst(p) = gather[p] when scatter_out, else p.
+struct TailReduceParams {
+    const char *ws;
+    char *out;
+    const int32_t *gather;
+    int64_t S;
+    int ldo, ncols;
+    bool scatter_out;
 };
 
 // n / d for 0 <= n < 2^31 as (umulhi(n, mul) + n) >> shift, d >= 1.
@@ -107,6 +133,7 @@ struct CombineBwdParams {
 
 hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream);
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream);
+int64_t dx_workspace_bytes(int64_t S, int E, int N, int K, int cus);
 hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream);
 
 // Split plan sizes: rows per chunk for a launch of S rows (0: no expert can

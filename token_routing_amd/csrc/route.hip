@@ -1,9 +1,9 @@
 // Routing metadata on the GPU: expert histogram, offsets (plain, padded,
 // tile) and the stable gather / scatter indices of the expert-grouped order.
 //
-// What is computed is the metadata the pages' grouped GEMMs consume: m_sizes
-// and "slicing gather_indices by cumsum of m_sizes" (grouped_gemm_forward
-// docstring, unsloth grouped_gemm/interface.py), expt_hist with its cumsum
+// What is computed is the metadata the pages' grouped GEMMs consume: m_sizes,
+// whose prefix sums cut the gather index into per-expert groups
+// (grouped_gemm_forward docstring, unsloth grouped_gemm/interface.py), expt_hist with its cumsum
 // offsets and block-padded offsets, and the inverse index pair of
 // GatherIndx / ScatterIndx (triton_kernels/matmul_ogs.py).
 //

@@ -368,7 +368,8 @@ KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "comb
                  ("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
                  ("dw_reduce_kernel", "dW_reduce"), ("tail_reduce_kernel", "tail_reduce"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),
-                 ("route_scan", "route_scan"), ("route_scatter", "route_scatter"))
+                 ("route_scan", "route_scan"), ("route_scatter", "route_scatter"),
+                 ("route_small", "route_small"))
 
 
 def _label(kernel_name):

@@ -214,6 +214,104 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(const int32_t *__
     }
 }
 
+// All three phases in one workgroup, for up to kSmallWaves chunks (a decode
+// step's few hundred slots): wave w counts chunk w into hist[w], the
+// workgroup turns the counts into per-chunk starts and the offsets, and wave
+// w then scatters chunk w from its cursors.  The same counting sort as the
+// three launches above, so the same bits, in one launch instead of three
+// (each a few microseconds of launch and drain on a decode step).
+constexpr int kSmallWaves = 16;
+constexpr int kSmallThreads = kSmallWaves * kWave;
+
+__global__ __launch_bounds__(kSmallThreads) void route_small(
+    const int32_t *__restrict__ ids, int64_t S, int E, int nbits, int block_m, int32_t *m_sizes,
+    int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets, int32_t *gather,
+    int32_t *scatter, int32_t *err)
+{
+    __shared__ int hist[kSmallWaves][kMaxExperts];  // counts, then chunk starts, then cursors
+    __shared__ int off[kMaxExperts];
+    __shared__ int poff[kMaxExperts];
+    __shared__ int toff[kMaxExperts];
+    __shared__ int totals[3];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t base = (int64_t)wave * kSlotsPerWave;
+    for (int e = lane; e < E; e += kWave)
+        hist[wave][e] = 0;
+    __syncthreads();
+    bool dropped = false;
+    for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
+        const int64_t s = base + step * kWave + lane;
+        const bool in = s < S;
+        const int id = in ? ids[s] : -1;
+        const bool valid = in && id >= 0 && id < E;
+        dropped |= in && !valid;
+        const uint64_t peers = same_id_lanes(id, valid, nbits);
+        if (valid && (peers & lanes_below()) == 0)
+            atomicAdd(&hist[wave][id], __popcll(peers));
+    }
+    if (dropped)
+        raise_error(err, kErrExpertId);
+    __syncthreads();
+    // Per expert: counts of the chunks before each chunk, and the total.
+    for (int e = threadIdx.x; e < E; e += kSmallThreads) {
+        int run = 0;
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int c = hist[w][e];
+            hist[w][e] = run;
+            run += c;
+        }
+        const int tiles = (run + block_m - 1) / block_m;
+        m_sizes[e] = run;
+        off[e] = run;
+        poff[e] = tiles * block_m;
+        toff[e] = tiles;
+    }
+    wave0_exclusive_scan(off, E, &totals[0]);
+    wave0_exclusive_scan(poff, E, &totals[1]);
+    wave0_exclusive_scan(toff, E, &totals[2]);
+    for (int e = threadIdx.x; e < E; e += kSmallThreads) {
+        offsets[e] = off[e];
+        if (padded_offsets)
+            padded_offsets[e] = poff[e];
+        if (tile_offsets)
+            tile_offsets[e] = toff[e];
+        for (int w = 0; w < kSmallWaves; ++w)
+            hist[w][e] += off[e];  // cursor of chunk w
+    }
+    if (threadIdx.x == 0) {
+        offsets[E] = totals[0];
+        if (padded_offsets)
+            padded_offsets[E] = totals[1];
+        if (tile_offsets)
+            tile_offsets[E] = totals[2];
+    }
+    for (int64_t p = totals[0] + threadIdx.x; p < S; p += kSmallThreads)
+        gather[p] = -1;  // positions left over by dropped slots
+    __syncthreads();
+    for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
+        const int64_t s = base + step * kWave + lane;
+        const bool in = s < S;
+        const int id = in ? ids[s] : -1;
+        const bool valid = in && id >= 0 && id < E;
+        const uint64_t peers = same_id_lanes(id, valid, nbits);
+        const uint64_t below = peers & lanes_below();
+        const int start = valid ? hist[wave][id] : 0;
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            const int pos = start + __popcll(below);
+            gather[pos] = (int32_t)s;
+            if (scatter)
+                scatter[s] = pos;
+            if (below == 0)
+                hist[wave][id] = start + __popcll(peers);
+        } else if (in && scatter) {
+            scatter[s] = -1;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 static int bits_for(int E)
 {
     int b = 0;
@@ -235,6 +333,12 @@ hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32
     const int nchunks = (int)route_chunks(S);
     const int nbits = bits_for(E);
     const int blocks = (nchunks + kRouteWaves - 1) / kRouteWaves;
+    if (nchunks <= kSmallWaves) {
+        hipLaunchKernelGGL(route_small, dim3(1), dim3(kSmallThreads), 0, stream, ids, S, E, nbits,
+                           block_m, m_sizes, offsets, padded_offsets, tile_offsets, gather,
+                           scatter, err);
+        return hipGetLastError();
+    }
     if (nchunks > 0) {
         hipLaunchKernelGGL(route_count, dim3(blocks), dim3(kRouteThreads), 0, stream, ids, S, E,
                            nbits, nchunks, counts, err);

@@ -1278,24 +1278,44 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
     const int64_t x_rows = px ? a.S / a.topk : a.S;
     const u32x4_t xr = rsrc_words(a.X, x_rows * row_bytes);
 
-    for (int t = xcd_logical_block(blockIdx.x, gridDim.x); t < total; t += gridDim.x) {
-        const int e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
+    // Tile t: expert, first sorted position, real rows, first column.
+    auto tile = [&](int t, int &e, int &p0, int &rows, int &n0) {
+        e = __builtin_amdgcn_readfirstlane(upper_index(s_tstart, a.E, t));
         const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1] - s_roff[e]);
-        const int p0base = __builtin_amdgcn_readfirstlane(s_roff[e]);
         const int mtiles = (mc + C::BM - 1) / C::BM;
         const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
-        const int mt = u % mtiles, nt = u / mtiles;
-        const int p0 = p0base + mt * C::BM;
-        const int rows = min(C::BM, mc - mt * C::BM);
-        const int n0 = nt * C::BN;
+        p0 = __builtin_amdgcn_readfirstlane(s_roff[e]) + (u % mtiles) * C::BM;
+        rows = min(C::BM, mc - (u % mtiles) * C::BM);
+        n0 = (u / mtiles) * C::BN;
+    };
+    // Gather entry of tile row threadIdx.x (one row per thread; -2: none).
+    // The next tile's entry is loaded before this tile's mainloop, so its
+    // latency is hidden; only the gate factor, which depends on it, is read
+    // when the tile starts.
+    static_assert(C::BM <= C::NT, "one tile row per thread");
+    auto fetch = [&](int p0, int rows) -> int {
+        const int i = threadIdx.x;
+        if (i >= C::BM || i >= rows)
+            return -2;
+        return (px || py) ? a.gather[p0 + i] : p0 + i;
+    };
 
-        for (int i = threadIdx.x; i < C::BM; i += C::NT) {
+    int t = xcd_logical_block(blockIdx.x, gridDim.x);
+    int e = 0, p0 = 0, rows = 0, n0 = 0, g = -2;
+    if (t < total) {
+        tile(t, e, p0, rows, n0);
+        g = fetch(p0, rows);
+    }
+    for (; t < total; t += gridDim.x) {
+        if (threadIdx.x < C::BM) {
+            const int i = threadIdx.x;
             int src = -1, dst = -1;
             float scale = 1.0f;
-            if (i < rows) {
+            if (g != -2) {
                 const int64_t p = p0 + i;
-                const int g = (px || py) ? checked_gather(a.gather, p, a.S, a.err) : (int)p;
-                if (g >= 0) {
+                if ((px || py) && (g < 0 || g >= a.S)) {
+                    raise_error(a.err, kErrGather);
+                } else {
                     src = px ? g / a.topk : (int)p;
                     dst = py ? g : (int)p;
                     if (fm)
@@ -1307,6 +1327,13 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             s_scale[i] = scale;
         }
         __syncthreads();
+        // The next tile's gather entries, in flight during this mainloop.
+        const int tn = t + gridDim.x;
+        int e_n = 0, p0_n = 0, rows_n = 0, n0_n = 0, g_n = -2;
+        if (tn < total) {
+            tile(tn, e_n, p0_n, rows_n, n0_n);
+            g_n = fetch(p0_n, rows_n);
+        }
 
         const u32x4_t wr =
             rsrc_words(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
@@ -1340,6 +1367,11 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             epilogue_gated<C>(st0, acc, s_dst, a.Y, a.N / 2, n0 / 2, a.N / 2);
         else
             epilogue_bf16<C, true>(st0, st1, acc, s_dst, s_scale, a.Y, a.N, n0, a.N);
+        e = e_n;
+        p0 = p0_n;
+        rows = rows_n;
+        n0 = n0_n;
+        g = g_n;
     }
 }
 

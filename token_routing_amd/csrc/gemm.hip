@@ -969,18 +969,55 @@ __device__ __forceinline__ int acc_col(int wn, int j)
 
 // bf16 epilogue through LDS.  The tile is staged as bf16 in st0 (or, when
 // it does not fit in one stage, rows [0, BM/2) in st0 and [BM/2, BM) in
-// st1), then copied out as 16-byte row segments.  Each lane addresses its
-// accumulators from one base pointer plus compile-time offsets.
+// st1), then copied out as 16-byte row segments.
 // s_dst[i]: destination row of tile row i (-1: skip); s_scale: per-row factor
 // applied when SCALE is set.  Y is bf16 with leading dimension ldy; tile
 // column c maps to output column n0 + c (valid below ncols).
+//
+// Staging layout: row-major, BN elements per row, with the 16-byte chunks of
+// row r permuted as chunk ^ 4 (r % 4).  An MFMA lane holds 4 adjacent rows of
+// one column; four adjacent lanes transpose their 4 x 4 values with two
+// cross-lane swaps (quad_transpose_bf16) so that each writes 4 adjacent
+// columns of one row as one 8-byte LDS write, a quarter of the writes of one
+// element at a time.  The permutation puts the four rows of a quad, 512
+// bytes apart, in different banks.
 template <class C>
 struct EpiLayout {
     static constexpr bool SPLIT = C::BM * C::BN * 2 > C::STAGE;
     static constexpr int ROWS_PER_BUF = SPLIT ? C::BM / 2 : C::BM;
     static_assert(ROWS_PER_BUF * C::BN * 2 <= C::STAGE, "staged rows must fit in one stage");
     static_assert(ROWS_PER_BUF % C::TM == 0, "a wave's rows must stay in one staging buffer");
+    static_assert(C::BN >= 128, "the chunk permutation needs 16 chunks per row");
+    // Byte offset of 16-byte chunk ch of staged row r.
+    __device__ __forceinline__ static int chunk_off(int r, int ch)
+    {
+        return r * C::BN * 2 + ((ch ^ ((r & 3) << 2)) << 4);
+    }
 };
+
+// Lanes 4q .. 4q + 3 hold x[k][c] (rows k = 0..3 in v0..v3, column c = lane
+// % 4).  Returns row lane % 4, columns 0..3, as packed bf16.  Swap 1 (lanes
+// c, c ^ 2) exchanges 2 x 2 blocks of row pairs; swap 2 (lanes c, c ^ 1)
+// exchanges single elements.  v_perm selects bytes of {S0, S1}, S1 low.
+__device__ __forceinline__ uint2 quad_transpose_bf16(float v0, float v1, float v2, float v3)
+{
+    const int k = threadIdx.x & 3;
+    const uint32_t d0 = pack_bf16x2(v0, v1), d1 = pack_bf16x2(v2, v3);
+    // Lanes 0, 1 keep rows 0-1 and receive them for columns + 2; lanes 2, 3
+    // keep rows 2-3 and receive them for columns - 2.
+    const bool low = (k & 2) == 0;
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(low ? d1 : d0), 0x4e,
+                                                              0xf, 0xf, false);
+    const uint32_t e0 = low ? d0 : r1, e1 = low ? r1 : d1;
+    // e0 = (x[a][c0], x[a+1][c0]), e1 = (x[a][c0+2], x[a+1][c0+2]) with c0 =
+    // the even column of the lane pair; the even lane wants row a, the odd
+    // lane row a + 1.
+    const bool even = (k & 1) == 0;
+    const uint32_t s2 = __builtin_amdgcn_perm(e1, e0, even ? 0x07060302u : 0x05040100u);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s2, 0xb1, 0xf, 0xf, false);
+    return {__builtin_amdgcn_perm(r2, e0, even ? 0x05040100u : 0x03020504u),
+            __builtin_amdgcn_perm(r2, e1, even ? 0x07060100u : 0x03020706u)};
+}
 
 // SCALE: multiply row i by s_scale[i].
 template <class C, bool SCALE>
@@ -992,23 +1029,42 @@ __device__ __forceinline__ void stage_bf16(char *st0, char *st1,
     const int wave = threadIdx.x / kWave;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int lane = threadIdx.x & (kWave - 1);
+    const int k = lane & 3;
+    // Accumulator row of v0 (register r % 4 == 0) for block row 0, group 0.
     const int row0 = wm * C::TM + 4 * (lane >> 5);
     char *buf = (wm * C::TM) / L::ROWS_PER_BUF ? st1 : st0;
-    uint16_t *base = reinterpret_cast<uint16_t *>(buf) +
-                     (row0 % L::ROWS_PER_BUF) * C::BN + wn * C::TN + (lane & 31);
+    // After the transpose this lane writes staged row row0 % RPB + k + 32 i +
+    // 8 g, columns wn * TN + 32 j + (lane & 28) + 0..3: the chunk part
+    // depends on j and k only (row % 4 == k), the row part is a constant.
+    char *rowp = buf + ((row0 % L::ROWS_PER_BUF) + k) * C::BN * 2;
+    int coff[C::FN];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+        const int ch = (wn * C::TN + j * 32) / 8 + ((lane >> 3) & 3);
+        coff[j] = ((ch ^ (k << 2)) << 4) + (lane & 4) * 2;
+    }
     const float *sc = s_scale + row0;
-    // Straight-line code, one output row of the wave's blocks at a time
-    // (sched_barrier): otherwise the compiler moves every accumulator out of
-    // the AGPRs, and loads every row factor, up front.
+    // Straight-line code, one group of 4 rows at a time (sched_barrier):
+    // otherwise the compiler moves every accumulator out of the AGPRs, and
+    // loads every row factor, up front.
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + 8 * (r >> 2) + (r & 3);  // row offset from row0
-            const float f = SCALE ? sc[rr] : 1.0f;
+        for (int g = 0; g < 4; ++g) {
+            const int rr = i * 32 + 8 * g;  // row offset of v0 from row0
+            float f[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if (SCALE) {
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                base[rr * C::BN + j * 32] = to_bf16(SCALE ? acc[i][j][r] * f : acc[i][j][r]);
+                for (int q = 0; q < 4; ++q)
+                    f[q] = sc[rr + q];
+            }
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const f32x16_t &a = acc[i][j];
+                const uint2 w = quad_transpose_bf16(a[4 * g] * f[0], a[4 * g + 1] * f[1],
+                                                    a[4 * g + 2] * f[2], a[4 * g + 3] * f[3]);
+                *reinterpret_cast<uint2 *>(rowp + rr * C::BN * 2 + coff[j]) = w;
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 }
@@ -1030,7 +1086,7 @@ __device__ __forceinline__ void epilogue_bf16(char *st0, char *st1,
         const char *buf = row / L::ROWS_PER_BUF ? st1 : st0;
         if (dst >= 0 && col < ncols)
             *reinterpret_cast<uint4 *>(Y + ((int64_t)dst * ldy + col) * 2) =
-                *reinterpret_cast<const uint4 *>(buf + ((row % L::ROWS_PER_BUF) * C::BN + ch * 8) * 2);
+                *reinterpret_cast<const uint4 *>(buf + L::chunk_off(row % L::ROWS_PER_BUF, ch));
     }
     __syncthreads();
 }

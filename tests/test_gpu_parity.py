@@ -278,6 +278,34 @@ def test_bwd_long_reduction(mg, flags, case):
         assert torch.count_nonzero(dW[e]).item() == 0
 
 
+# dW over experts of more than 1024 rows without the split workspace: the
+# reduction then crosses the 1024-row segments in which gather entries are
+# staged, and ends in a ragged 32-row slot.  K = 72 and N = 264 leave ragged
+# output tiles.
+DW_LONG_ROWS = [(1100, 72, 264, 2, 2, 16, ()), (1500, 136, 136, 3, 2, 17, (1,))]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])
+@pytest.mark.parametrize("case", DW_LONG_ROWS,
+                         ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in DW_LONG_ROWS])
+def test_dw_long_rows_unsplit(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty, with_dy=True)
+    r = _gpu_route(mg, wl)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    assert ref_route["m_sizes"].max() > 1024
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dW = mg.grouped_gemm_dW(_dev(wl.X), _dev(wl.dY), r["m_sizes"], r["gather"], wl.topk, flags,
+                            split=False, error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = oracle.grouped_gemm_dW(synth.bits(wl.X), synth.bits(wl.dY), ref_route["m_sizes"],
+                                 ref_route["gather"], wl.topk, flags, E)
+    _assert_close(dW.reshape(E * N, K).float().cpu().numpy(), ref, f"dW {case} flags={flags}")
+    for e in empty:
+        assert torch.count_nonzero(dW[e]).item() == 0
+
+
 def test_bwd_mixtral_sampled(mg):
     wl = synth.mixtral()
     wl.dY = synth.normal_bf16((wl.S, wl.N), 0.01, synth.generator(synth.SEEDS["mixtral_bwd_dy"]))

@@ -291,13 +291,15 @@ struct RowTileLoader {
 // requested, and every prepare of a stage runs before its first copy is
 // issued: the compiler (which does not see the copies) may insert a wait for
 // the raw loads there, and at that point nothing else is in flight.
-template <int COLS, int NT>
+//
+// D: reduction rows per LDS stage (BK, or a shorter slot).
+template <int COLS, int NT, int D = BK>
 struct TileDmaLoader {
     static constexpr int CPR = COLS / 8;
     static constexpr int RW = kWave / CPR;
     static constexpr int NWAVE = NT / kWave;
-    static constexpr int RPT = BK / (RW * NWAVE);
-    static_assert(kWave % CPR == 0 && BK % (RW * NWAVE) == 0, "whole windows per stage");
+    static constexpr int RPT = D / (RW * NWAVE);
+    static_assert(kWave % CPR == 0 && D % (RW * NWAVE) == 0, "whole windows per stage");
     static_assert(COLS >= 128, "the row swizzle needs 16 chunks per row");
     int32_t raw[RPT];
     int red0 = 0;
@@ -332,6 +334,24 @@ struct TileDmaLoader {
         for (int i = 0; i < RPT; ++i) {
             const int row = row_of(i);
             const int idx = fin(red0 + row, raw[i]);
+            const int col = col0 + (pc ^ ((row & 3) << 2)) * 8;
+            voff[i] = (idx >= 0 && col < ncols)
+                          ? (uint32_t)idx * (uint32_t)row_bytes + (uint32_t)col * 2
+                          : kOOB;
+        }
+    }
+
+    // One-phase form: rowfn(row) -> HBM row of tile row `row` (-1: zeros),
+    // for row indices that need no memory load of their own.
+    template <class RowFn>
+    __device__ __forceinline__ void prepare_rows(int col0, int ncols, int64_t row_bytes,
+                                                 RowFn rowfn)
+    {
+        const int pc = (int)(threadIdx.x % kWave) % CPR;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = row_of(i);
+            const int idx = rowfn(row);
             const int col = col0 + (pc ^ ((row & 3) << 2)) * 8;
             voff[i] = (idx >= 0 && col < ncols)
                           ? (uint32_t)idx * (uint32_t)row_bytes + (uint32_t)col * 2
@@ -1596,6 +1616,34 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
 
 constexpr int kGroupK = 8;
 
+// The dW reduction runs over rows, so each step's rows (and, under a permute
+// flag, their gather entries) are new, and the copies of a 64-row stage take
+// longer to land than the MFMAs of the previous stage run: with MFMAs
+// removed, the two-stage loop still takes 1.5 us per stage on the Mixtral
+// shape, against 0.95 us per stage with the copies removed.  dW therefore
+// splits the same 128 KiB of LDS into four 32-row slots and issues each
+// slot's copies three slots ahead.  Gather entries are staged in LDS for a
+// segment of up to kDwGather rows at a time, so that the only vector-memory
+// operations in the loop are the copies and each wait can count them.
+#ifndef MOEGG_DW_SLOTS
+#define MOEGG_DW_SLOTS 1
+#endif
+constexpr int kDwSlot = 32;      // reduction rows per slot
+constexpr int kDwSlots = 4;
+constexpr int kDwGather = 1024;  // gather entries staged per segment
+
+// MFMAs of one 32-row slot (both operands reduction rows in LDS).
+template <class C>
+__device__ __forceinline__ void dw_slot_mma(const char *As, const char *Bs,
+                                            f32x16_t (&acc)[C::FM][C::FN], int wm, int wn)
+{
+    bf16x8_t a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+    read_step<C, true, true>(As, Bs, 0, wm, wn, a0, b0);
+    read_step<C, true, true>(As, Bs, 1, wm, wn, a1, b1);
+    mma_step<C>(a0, b0, acc);
+    mma_step<C>(a1, b1, acc);
+}
+
 
 // PX / PY: the forward's permute flags, as template parameters so that the
 // per-stage row-index code has no flag branches.
@@ -1711,7 +1759,86 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         const int nsteps = (mc + BK - 1) / BK;
-        if constexpr (MOEGG_TILE_DMA != 0) {
+        if constexpr (MOEGG_TILE_DMA != 0 && MOEGG_DW_SLOTS != 0) {
+            static_assert(kDwSlots * 2 * C::BM * kDwSlot * 2 <= 2 * C::STAGE &&
+                              C::BM == C::BN && kMaxExperts + 1 >= kDwGather,
+                          "four slots in the two stages; gather entries in s_tstart");
+            constexpr int SLOT_A = C::BM * kDwSlot * 2, SLOT = 2 * SLOT_A;
+            int *const s_g = s_tstart;  // free once the plan is built
+            const FastDiv tdiv = a.topk_div;
+            const uint32_t Su = (uint32_t)S;
+            const int wave = threadIdx.x / kWave;
+            const int wm = wave / C::WN, wn = wave % C::WN;
+            bool bad = false;
+            TileDmaLoader<C::BM, C::NT, kDwSlot> la;
+            TileDmaLoader<C::BN, C::NT, kDwSlot> lb;
+            constexpr int NC = TileDmaLoader<C::BM, C::NT, kDwSlot>::RPT +
+                               TileDmaLoader<C::BN, C::NT, kDwSlot>::RPT;  // copies per wave per slot
+            for (int seg0 = 0; seg0 < mc; seg0 += kDwGather) {
+                const int segn = min(kDwGather, mc - seg0);
+                const int ns = (segn + kDwSlot - 1) / kDwSlot;
+                if constexpr (PX || PY) {
+                    for (int i = threadIdx.x; i < segn; i += C::NT)
+                        s_g[i] = gather[start + seg0 + i];
+                    __syncthreads();
+                } else {
+                    wait_vmem();  // earlier stores: the waits below count copies only
+                }
+                // HBM rows of segment row r (-1: zeros).  A gather entry
+                // outside [0, S) gives zeros and is reported once per tile.
+                auto dyrow = [&](int r) -> int {
+                    const bool in = r < segn;
+                    if constexpr (PY) {
+                        const int g = s_g[min(r, segn - 1)];
+                        const bool ok = (uint32_t)g < Su;
+                        bad |= in && !ok;
+                        return in && ok ? g : -1;
+                    }
+                    return in ? start + seg0 + r : -1;
+                };
+                auto xrow = [&](int r) -> int {
+                    const bool in = r < segn;
+                    if constexpr (PX) {
+                        const int g = s_g[min(r, segn - 1)];
+                        const bool ok = (uint32_t)g < Su;
+                        bad |= in && !ok;
+                        return in && ok ? fast_div((uint32_t)g, tdiv) : -1;
+                    }
+                    return in ? start + seg0 + r : -1;
+                };
+                auto issue = [&](int q) {
+                    char *sl = smem + (q % kDwSlots) * SLOT;
+                    la.prepare_rows(n0, a.N, dy_row, [&](int row) { return dyrow(q * kDwSlot + row); });
+                    lb.prepare_rows(k0, a.K, x_row, [&](int row) { return xrow(q * kDwSlot + row); });
+                    __builtin_amdgcn_sched_barrier(0);
+                    la.issue(dyr, sl);
+                    lb.issue(xr, sl + SLOT_A);
+                };
+                for (int q = 0; q < min(ns, kDwSlots - 1); ++q)
+                    issue(q);
+                for (int q = 0; q < ns; ++q) {
+                    // Slot q's copies are complete once at most the copies of
+                    // the (up to two) slots issued after it are in flight.
+                    const int after = min(kDwSlots - 2, ns - 1 - q);
+                    if (after >= 2)
+                        wait_vmcnt<2 * NC>();
+                    else if (after == 1)
+                        wait_vmcnt<NC>();
+                    else
+                        wait_vmcnt<0>();
+                    wait_lds();
+                    wg_barrier();
+                    // Every wave is past slot q - 1, whose buffer slot q + 3 reuses.
+                    if (q + kDwSlots - 1 < ns)
+                        issue(q + kDwSlots - 1);
+                    const char *sl = smem + (q % kDwSlots) * SLOT;
+                    dw_slot_mma<C>(sl, sl + SLOT_A, acc, wm, wn);
+                }
+                __syncthreads();  // slots and s_g free for the next segment or the epilogue
+            }
+            if (bad)
+                raise_error(err, kErrGather);
+        } else if constexpr (MOEGG_TILE_DMA != 0) {
             // Row index of reduction index red in dY and in X (-1: zeros),
             // without branches.  raw: the gather entry (read clamped into the
             // expert's rows) or the sorted position; fin: validity and, for

@@ -995,12 +995,20 @@ __device__ __forceinline__ int acc_col(int wn, int j)
 // column c maps to output column n0 + c (valid below ncols).
 //
 // Staging layout: row-major, BN elements per row, with the 16-byte chunks of
-// row r permuted as chunk ^ 4 (r % 4).  An MFMA lane holds 4 adjacent rows of
-// one column; four adjacent lanes transpose their 4 x 4 values with two
-// cross-lane swaps (quad_transpose_bf16) so that each writes 4 adjacent
-// columns of one row as one 8-byte LDS write, a quarter of the writes of one
-// element at a time.  The permutation puts the four rows of a quad, 512
-// bytes apart, in different banks.
+// row r permuted as chunk ^ g(r % 4), g(k) = 2k ^ 4k (0, 6, 12, 10).  An MFMA
+// lane holds 4 adjacent rows of one column; four adjacent lanes transpose
+// their 4 x 4 values with two cross-lane swaps (quad_transpose_bf16) so that
+// each writes 4 adjacent columns of one row as one 8-byte LDS write, a
+// quarter of the writes of one element at a time.  The four rows of a quad
+// are 512 bytes apart; g gives each of them a different 32-byte bank group
+// within 128 bytes (bits 1-2 of g distinct) and a different 64-byte group
+// within 256 bytes (bits 2-3 distinct).  With chunk ^ 4k alone, only the
+// latter held and the SQ counters showed 4-30% of LDS cycles in conflicts.
+__device__ __forceinline__ int quad_perm(int k)
+{
+    return (k << 1) ^ (k << 2);
+}
+
 template <class C>
 struct EpiLayout {
     static constexpr bool SPLIT = C::BM * C::BN * 2 > C::STAGE;
@@ -1011,7 +1019,7 @@ struct EpiLayout {
     // Byte offset of 16-byte chunk ch of staged row r.
     __device__ __forceinline__ static int chunk_off(int r, int ch)
     {
-        return r * C::BN * 2 + ((ch ^ ((r & 3) << 2)) << 4);
+        return r * C::BN * 2 + ((ch ^ quad_perm(r & 3)) << 4);
     }
 };
 
@@ -1061,7 +1069,7 @@ __device__ __forceinline__ void stage_bf16(char *st0, char *st1,
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) {
         const int ch = (wn * C::TN + j * 32) / 8 + ((lane >> 3) & 3);
-        coff[j] = ((ch ^ (k << 2)) << 4) + (lane & 4) * 2;
+        coff[j] = ((ch ^ quad_perm(k)) << 4) + (lane & 4) * 2;
     }
     const float *sc = s_scale + row0;
     // Straight-line code, one group of 4 rows at a time (sched_barrier):

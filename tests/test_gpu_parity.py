@@ -141,6 +141,8 @@ FWD_SMALL = [
     (700, 136, 520, 6, 3, 2, (0,)),       # K not a multiple of 64, N not of 256
     (64, 256, 512, 16, 4, 3, (2, 9)),     # avg 16 rows -> small-tile path
     (33, 64, 136, 40, 8, 4, (1, 5, 39)),  # tiny groups, many empty experts
+    (40, 136, 264, 4, 4, 5, ()),          # avg 40 rows: two 32-row blocks per expert,
+                                          # K = 8.5 steps of 16, a ragged 32-column block
 ]
 
 

@@ -1340,6 +1340,25 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduceParams a)
 
 // GATED: W rows come in (gate, linear) pairs and Y gets N/2 columns of the
 // gated activation (epilogue_gated).
+// Raster of an expert's output tiles: tile u of mt row tiles x nt column
+// tiles.  The row tiles are taken in bands of up to kBandM; within a band
+// the row tiles of one column tile are consecutive.  An XCD's 32 concurrent
+// tiles then cover at most 8 row tiles and 4 or more column tiles: on a
+// dense 8192 x 28672 x 4096 product, 32 row tiles of one column tile made
+// each stage fetch 33 distinct slices into the XCD's L2 instead of 12.
+// Experts of up to kBandM row tiles keep the plain column-major order.
+constexpr int kBandM = 8;
+
+__device__ __forceinline__ void band_raster(int u, int mt, int nt, int &m, int &n)
+{
+    const int band = u / (kBandM * nt);
+    const int first = band * kBandM;
+    const int gm = min(mt - first, kBandM);
+    const int r = u - band * kBandM * nt;
+    m = first + r % gm;
+    n = r / gm;
+}
+
 template <class C, bool GATED>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 {
@@ -1368,9 +1387,11 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
         const int mc = __builtin_amdgcn_readfirstlane(s_roff[e + 1] - s_roff[e]);
         const int mtiles = (mc + C::BM - 1) / C::BM;
         const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
-        p0 = __builtin_amdgcn_readfirstlane(s_roff[e]) + (u % mtiles) * C::BM;
-        rows = min(C::BM, mc - (u % mtiles) * C::BM);
-        n0 = (u / mtiles) * C::BN;
+        int mt, nt;
+        band_raster(u, mtiles, ntn, mt, nt);
+        p0 = __builtin_amdgcn_readfirstlane(s_roff[e]) + mt * C::BM;
+        rows = min(C::BM, mc - mt * C::BM);
+        n0 = nt * C::BN;
     };
     // Gather entry of tile row threadIdx.x (one row per thread; -2: none).
     // The next tile's entry is loaded before this tile's mainloop, so its
@@ -1496,7 +1517,8 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         const int p0base = __builtin_amdgcn_readfirstlane(s_roff[e]);
         const int mtiles = (mc + C::BM - 1) / C::BM;
         const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
-        const int mt = u % mtiles, kt = u / mtiles;
+        int mt, kt;
+        band_raster(u, mtiles, ntk, mt, kt);
         const int p0 = p0base + mt * C::BM;
         const int rows = min(C::BM, mc - mt * C::BM);
         const int k0 = kt * C::BN;

@@ -308,6 +308,30 @@ def test_dw_long_rows_unsplit(mg, flags, case):
         assert torch.count_nonzero(dW[e]).item() == 0
 
 
+# Experts of more than 8 row tiles of 256 are rastered in bands of 8 row tiles
+# (forward over N tiles, dX over K tiles): 2 experts of 2200 rows give a full
+# band of 8 and a ragged band of 1, with ragged column tiles on both sides.
+BANDED = [(2200, 520, 264, 2, 2, 18, ())]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])
+@pytest.mark.parametrize("case", BANDED, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in BANDED])
+def test_banded_raster_long_experts(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty, with_dy=True)
+    got, ref, _ = _fwd_case(mg, wl, flags)
+    _assert_close(got, ref, f"fwd {case} flags={flags}")
+    r = _gpu_route(mg, wl)
+    ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, 128)
+    assert ref_route["m_sizes"].min() > 8 * 256
+    for split in (False, True):
+        dX = mg.grouped_gemm_dX(_dev(wl.dY), _dev(wl.W), r["m_sizes"], r["gather"], wl.topk,
+                                flags, split=split)
+        ref_dx = oracle.grouped_gemm_dX(synth.bits(wl.dY), synth.bits(wl.W),
+                                        ref_route["m_sizes"], ref_route["gather"], wl.topk, flags)
+        _assert_close(dX.float().cpu().numpy(), ref_dx, f"dX {case} flags={flags} split={split}")
+
+
 def test_bwd_mixtral_sampled(mg):
     wl = synth.mixtral()
     wl.dY = synth.normal_bf16((wl.S, wl.N), 0.01, synth.generator(synth.SEEDS["mixtral_bwd_dy"]))

@@ -145,3 +145,24 @@ def test_combine_fine_shape(mg):
     _ok(dY.float().cpu().numpy(), dY_ref, "dY fine")
     ok, info = bf16_tolerance_ok(dw.cpu().numpy(), dw_ref, rel_fro_max=1e-5, max_elem=1e-3)
     assert ok, info
+
+
+@pytest.mark.parametrize("case", [(300, 136, 264, 5, 2, 51), (96, 520, 136, 8, 4, 52)],
+                         ids=["T300K136N264k2", "T96K520N136k4"])
+def test_first_gemm_backward_token_gradient(mg, case):
+    """Backward of the first MoE GEMM (forward with permute_x): dX scattered to
+    slot order by moegg_grouped_gemm_dX, then summed over each token's k
+    slots by the unweighted combine, gives the gradient of the token rows X."""
+    T, K, N, E, topk, seed = case
+    wl = synth.random_case(T, K, N, E, topk, synth.PERMUTE_X, seed, with_dy=True)
+    r = oracle.route(wl.ids.numpy().reshape(-1), E, 128)
+    g = mg.moe_route(wl.ids.cuda(), E, 128)
+    dX = mg.grouped_gemm_dX(wl.dY.cuda(), wl.W.cuda(), g["m_sizes"], g["gather"], topk,
+                            synth.PERMUTE_X)
+    dXt = mg.combine(dX, topk)
+    torch.cuda.synchronize()
+    assert dXt.shape == (T, K)
+    ref_slots = oracle.grouped_gemm_dX(synth.bits(wl.dY), synth.bits(wl.W), r["m_sizes"],
+                                       r["gather"], topk, synth.PERMUTE_X)
+    ref = ref_slots.astype(np.float64).reshape(T, topk, K).sum(axis=1)
+    _ok(dXt.float().cpu().numpy(), ref.astype(np.float32), f"token gradient {case}")

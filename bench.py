@@ -197,6 +197,8 @@ def make_step(name):
                                 rotate=4)
     if name == "tiny":
         return build_layer_step(synth.tiny(), dY_seed=0, with_bwd=False)
+    if name == "dense":
+        return build_layer_step(synth.dense(), dY_seed=0, with_bwd=False)
     if name == "dual":
         return build_dual_step(synth.dual())
     if name == "combine":
@@ -217,6 +219,9 @@ WORKLOAD_DESC = {
     "decode_bwd": "decode-shaped backward of the fine-grained down GEMM, T=64 E=128 top-8 K=768 "
                   "N=2048; step = route + fwd(permute_y) + dX + dW",
     "dual": "asymmetric dual-expert GEMM: [512,1024]x[1024,2048] and [256,1024]x[1024,4096]",
+    "dense": "the Mixtral gate_up FLOPs as one dense product through the grouped forward: "
+             "X [8192,4096] times W^T, W [28672,4096] (one expert); the line also times the "
+             "vendor GEMM (hipBLASLt via torch.matmul) on the same operands",
     "tiny": "tiny MoE grouped GEMM, T=128 K=256 N=512 E=8 top-2, permute_x",
     "combine": "top-k combine after the fine-grained down projection, T=8192 top-8 N=2048 "
                "(expert-sorted Y, routing weights) and its backward with the weight gradient",
@@ -351,6 +356,27 @@ def cpu_baseline(st, budget_s):
             "seconds": round(dt, 3)}
 
 
+def vendor_reference(st, steps, warmup):
+    """hipBLASLt (torch.matmul) on the dense workload's operands, timed like a
+    step: a reference point for the forward's kernel, not part of the path."""
+    wl = st.inputs
+    X = _dev(wl.X)
+    Wt = _dev(wl.W[0]).t()
+    for _ in range(warmup):
+        torch.matmul(X, Wt)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        torch.matmul(X, Wt)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    flops = 2.0 * wl.T * wl.N * wl.K
+    return {"kernel": "hipBLASLt via torch.matmul(X, W.t())", "ms": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters: each launch reads and writes nbytes."""
@@ -369,7 +395,7 @@ KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "comb
                  ("dw_reduce_kernel", "dW_reduce"), ("tail_reduce_kernel", "tail_reduce"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),
                  ("route_scan", "route_scan"), ("route_scatter", "route_scatter"),
-                 ("route_small", "route_small"))
+                 ("route_small", "route_small"), ("Cijk_", "vendor"))
 
 
 def _label(kernel_name):
@@ -422,7 +448,7 @@ def counter_lines(sq_dir, stat_rows):
            "run's average duration, indicative only since the runs differ):", "",
            "| kernel | MFMA busy | LDS bank conflicts / LDS active | clock GHz (indicative) |",
            "|---|---|---|---|"]
-    for lab in ("fwd", "dX", "dW", "groups", "combine", "combine_bwd"):
+    for lab in ("fwd", "dX", "dW", "groups", "combine", "combine_bwd", "vendor"):
         g = means["GRBM_GUI_ACTIVE"].get(lab)
         if not g or lab not in dur:
             continue
@@ -431,6 +457,26 @@ def counter_lines(sq_dir, stat_rows):
         act = means["SQ_LDS_IDX_ACTIVE"].get(lab, 0.0)
         conf = means["SQ_LDS_BANK_CONFLICT"].get(lab, 0.0) / act if act else 0.0
         out.append(f"| {lab} | {100 * busy:.1f}% | {conf:.4f} | {cyc / dur[lab]:.2f} |")
+    return out
+
+
+def memory_lines(l2_dir, tcp_dir):
+    """Per-kernel L2 hit rate (TCC_HIT_sum, TCC_MISS_sum) and mean L1 -> L2
+    read latency (TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum), each
+    pass in its own run."""
+    import glob
+    f2 = glob.glob(os.path.join(l2_dir, "*counter_collection.csv"))[0]
+    fp = glob.glob(os.path.join(tcp_dir, "*counter_collection.csv"))[0]
+    hit, miss = _counter_means(f2, "TCC_HIT_sum"), _counter_means(f2, "TCC_MISS_sum")
+    ea = _counter_means(f2, "TCC_EA0_RDREQ_sum")
+    lat, req = _counter_means(fp, "TCP_TCC_READ_REQ_LATENCY_sum"), _counter_means(fp, "TCP_TCC_READ_REQ_sum")
+    out = ["", "L2 and L1 -> L2 counters (two more passes; per launch):", "",
+           "| kernel | L1 -> L2 read requests | L2 hit rate | L2 -> fabric read requests | "
+           "mean L1 -> L2 read latency (cycles) |", "|---|---|---|---|---|"]
+    for lab in ("fwd", "dX", "dW", "groups", "vendor"):
+        if lab in hit and lab in req and req[lab]:
+            out.append(f"| {lab} | {req[lab]:.3g} | {hit[lab] / (hit[lab] + miss[lab]):.3f} | "
+                       f"{ea.get(lab, 0.0):.3g} | {lat[lab] / req[lab]:.0f} |")
     return out
 
 
@@ -482,6 +528,8 @@ def summarize(prof_dir, workload, command):
     sq_dir = os.path.join(prof_dir, "sq")
     if os.path.isdir(sq_dir):
         lines += counter_lines(sq_dir, rows)
+    if os.path.isdir(os.path.join(prof_dir, "l2")) and os.path.isdir(os.path.join(prof_dir, "tcp")):
+        lines += memory_lines(os.path.join(prof_dir, "l2"), os.path.join(prof_dir, "tcp"))
     out = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print(out)
@@ -547,6 +595,7 @@ def main():
                 "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(args.workload, label)}
 
+    vendor = vendor_reference(st, args.steps, args.warmup) if args.workload == "dense" else None
     cpu = cpu_baseline(st, args.cpu_budget) if args.cpu_budget > 0 else None
     line = {
         "metric": "MoE grouped-GEMM useful TFLOP/s (bf16) + % of MFMA/HBM roofline, fwd/dX/dW",
@@ -556,6 +605,7 @@ def main():
         "config": {"workload": args.workload, "desc": WORKLOAD_DESC[args.workload],
                    "block_m_route": BLOCK_M},
         "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
+        **({"vendor_reference": vendor} if vendor else {}),
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

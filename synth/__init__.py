@@ -42,7 +42,8 @@ FUSE_MUL_POST = 4
 
 # Seeds: 1000 + the workload's number; the decode slice and dY have their own.
 SEEDS = {"tiny": 1001, "dual": 1002, "mixtral": 1003, "fine_down": 1004,
-         "fine_bwd_dy": 1005, "fine_decode": 1041, "mixtral_bwd_dy": 2003, "combine_y": 1046}
+         "fine_bwd_dy": 1005, "fine_decode": 1041, "mixtral_bwd_dy": 2003, "combine_y": 1046,
+         "dense": 1007}
 
 
 def generator(seed: int) -> torch.Generator:
@@ -146,6 +147,18 @@ def mixtral(T=4096, K=4096, N=28672, E=8, topk=2, seed=SEEDS["mixtral"]) -> Work
     X = normal_bf16((T, K), 1.0, g)
     W = normal_bf16((E, N, K), 0.02, g)
     return Workload("mixtral", T, K, N, E, topk, PERMUTE_X, ids, w, X, W)
+
+
+def dense(T=8192, K=4096, N=28672, seed=SEEDS["dense"]) -> Workload:
+    """The Mixtral gate_up FLOPs as one dense product (a single expert, every
+    row routed to it, no permutation): the shape on which the grouped kernels
+    are compared with a vendor GEMM."""
+    g = generator(seed)
+    ids = torch.zeros(T, 1, dtype=torch.int32)
+    w = torch.ones(T, 1, dtype=torch.float32)
+    X = normal_bf16((T, K), 1.0, g)
+    W = normal_bf16((1, N, K), 0.02, g)
+    return Workload("dense", T, K, N, 1, 1, 0, ids, w, X, W)
 
 
 def _fine(name, T, K, N, E, topk, s, seed, rank_seed, with_dy):

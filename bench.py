@@ -213,9 +213,11 @@ WORKLOAD_DESC = {
                      "epilogue, T=4096 K=4096 N=28672 (-> 14336) E=8 top-2, permute_x; "
                      "step = route + fwd",
     "fine": "fine-grained MoE down grouped GEMM, T=8192 E=128 top-8 K=768 N=2048 Zipf(1.2); "
-            "step = route + fwd(permute_y+fuse_mul_post) + dX + dW",
-    "fine_fwd": "fine-grained MoE down grouped GEMM forward, T=8192 E=128 top-8 K=768 N=2048",
-    "decode": "fine-grained MoE down grouped GEMM decode slice, T=64 E=128 top-8 K=768 N=2048",
+            "training step = route + fwd(permute_y) + dX + dW (dY gathered on load)",
+    "fine_fwd": "fine-grained MoE down grouped GEMM forward, T=8192 E=128 top-8 K=768 N=2048, "
+                "permute_y + fuse_mul_post",
+    "decode": "fine-grained MoE down grouped GEMM decode slice, T=64 E=128 top-8 K=768 N=2048, "
+              "permute_y + fuse_mul_post",
     "decode_bwd": "decode-shaped backward of the fine-grained down GEMM, T=64 E=128 top-8 K=768 "
                   "N=2048; step = route + fwd(permute_y) + dX + dW",
     "dual": "asymmetric dual-expert GEMM: [512,1024]x[1024,2048] and [256,1024]x[1024,4096]",

@@ -127,6 +127,7 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
     st.m_sizes = m_sizes
     st.flags = flags
     st.inputs = wl
+    st.dY_seed = dY_seed
     return st
 
 
@@ -358,25 +359,66 @@ def cpu_baseline(st, budget_s):
             "seconds": round(dt, 3)}
 
 
-def vendor_reference(st, steps, warmup):
-    """hipBLASLt (torch.matmul) on the dense workload's operands, timed like a
-    step: a reference point for the forward's kernel, not part of the path."""
-    wl = st.inputs
-    X = _dev(wl.X)
-    Wt = _dev(wl.W[0]).t()
+def _time(fn, steps, warmup):
     for _ in range(warmup):
-        torch.matmul(X, Wt)
+        fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
-        torch.matmul(X, Wt)
+        fn()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
-    flops = 2.0 * wl.T * wl.N * wl.K
-    return {"kernel": "hipBLASLt via torch.matmul(X, W.t())", "ms": round(ms, 4),
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    return a.elapsed_time(b) / steps
+
+
+def vendor_reference(st, steps, warmup):
+    """hipBLASLt (torch.matmul) on the same products, timed like a step: a
+    reference point for the kernels, not part of the path.
+
+    dense: one product X W^T.  Routed layer workloads: the products expert by
+    expert (one torch.matmul per expert and kernel), on operands gathered
+    into expert order beforehand (the gathers are not timed)."""
+    wl = st.inputs
+    if st.name == "dense":
+        X = _dev(wl.X)
+        Wt = _dev(wl.W[0]).t()
+        ms = _time(lambda: torch.matmul(X, Wt), steps, warmup)
+        flops = 2.0 * wl.T * wl.N * wl.K
+        return {"kernel": "hipBLASLt via torch.matmul(X, W.t())", "ms": round(ms, 4),
+                "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    if not hasattr(st, "dY_seed"):
+        return None                     # not a routed grouped-GEMM workload
+    E, N, K = wl.W.shape
+    route = mg.moe_route(_dev(wl.ids), E, BLOCK_M)
+    torch.cuda.synchronize()
+    off = route["offsets"].cpu().numpy()
+    g = route["gather"].long()
+    px = bool(wl.flags & synth.PERMUTE_X)
+    py = bool(wl.flags & synth.PERMUTE_Y)
+    X = _dev(wl.X)
+    X = X[g // wl.topk] if px else X                        # expert order
+    W = _dev(wl.W)
+    out = {"kernel": "hipBLASLt via torch.matmul, one call per expert and product",
+           "note": "operands gathered into expert order outside the timed region"}
+    experts = [(e, int(off[e]), int(off[e + 1])) for e in range(E) if off[e + 1] > off[e]]
+    flops = 2.0 * float(off[E]) * N * K
+    Y = torch.empty(int(off[E]), N, dtype=torch.bfloat16, device="cuda")
+    ms = _time(lambda: [torch.matmul(X[lo:hi], W[e].t(), out=Y[lo:hi]) for e, lo, hi in experts],
+               steps, warmup)
+    out["fwd"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    if any(lab == "dX" for lab, _, _, _ in st.kernels):
+        dY = synth.normal_bf16((wl.S, N), 0.01, synth.generator(st.dY_seed)).to("cuda")
+        dY = dY[g] if py else dY                              # expert order
+        dX = torch.empty(int(off[E]), K, dtype=torch.bfloat16, device="cuda")
+        dW = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
+        ms = _time(lambda: [torch.matmul(dY[lo:hi], W[e], out=dX[lo:hi]) for e, lo, hi in experts],
+                   steps, warmup)
+        out["dX"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        ms = _time(lambda: [torch.matmul(dY[lo:hi].t(), X[lo:hi], out=dW[e])
+                            for e, lo, hi in experts], steps, warmup)
+        out["dW"] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+    return out
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -548,6 +590,9 @@ def main():
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_DESC))
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of CPU oracle work for the baseline (0 disables)")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time hipBLASLt (torch.matmul) on the same products, expert by "
+                         "expert (always on for --workload dense)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize", metavar="PROF_DIR",
@@ -597,7 +642,8 @@ def main():
                 "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(args.workload, label)}
 
-    vendor = vendor_reference(st, args.steps, args.warmup) if args.workload == "dense" else None
+    vendor = (vendor_reference(st, args.steps, args.warmup)
+              if args.workload == "dense" or args.vendor else None)
     cpu = cpu_baseline(st, args.cpu_budget) if args.cpu_budget > 0 else None
     line = {
         "metric": "MoE grouped-GEMM useful TFLOP/s (bf16) + % of MFMA/HBM roofline, fwd/dX/dW",

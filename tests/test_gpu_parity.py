@@ -280,11 +280,12 @@ def test_bwd_long_reduction(mg, flags, case):
         assert torch.count_nonzero(dW[e]).item() == 0
 
 
-# dW over experts of more than 1024 rows without the split workspace: the
-# reduction then crosses the 1024-row segments in which gather entries are
-# staged, and ends in a ragged 32-row slot.  K = 72 and N = 264 leave ragged
-# output tiles.
-DW_LONG_ROWS = [(1100, 72, 264, 2, 2, 16, ()), (1500, 136, 136, 3, 2, 17, (1,))]
+# dW over long experts without the split workspace: the reduction crosses
+# the 1024-row segments in which gather entries are staged (two segments for
+# 1100 and 1500 rows, three for 2200) and ends in a ragged 32-row slot.
+# K = 72 and N = 264 leave ragged output tiles.
+DW_LONG_ROWS = [(1100, 72, 264, 2, 2, 16, ()), (1500, 136, 136, 3, 2, 17, (1,)),
+                (2200, 72, 264, 2, 2, 19, ())]
 
 
 @pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])

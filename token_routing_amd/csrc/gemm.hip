@@ -1301,13 +1301,20 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduceParams a)
     const float4 *partials = reinterpret_cast<const float4 *>(a.ws + tail_header_bytes());
     const int R = hdr[0], P = hdr[1];
     constexpr int Q = BN / 4;  // float4 per tile row
-    for (int r = 0; r < R; ++r) {
+    // All tiles' items at once (one tile at a time left most threads idle
+    // and made the launch a chain of R memory round trips).  A block's 256
+    // consecutive items lie in one tile, so the tile's header is uniform.
+    constexpr int PER = BM * Q;  // items per tile
+    static_assert(PER % 256 == 0, "a block's items stay in one tile");
+    for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < (int64_t)R * PER;
+         w += (int64_t)gridDim.x * blockDim.x) {
+        const int r = __builtin_amdgcn_readfirstlane((int)(w / PER));
         const int p0 = hdr[2 + 4 * r], rows = hdr[3 + 4 * r], c0 = hdr[4 + 4 * r];
-        for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < rows * Q;
-             idx += gridDim.x * blockDim.x) {
+        {
+            const int idx = (int)(w % PER);
             const int i = idx / Q, j = idx % Q;
             const int col = c0 + 4 * j;
-            if (col >= a.ncols)
+            if (i >= rows || col >= a.ncols)
                 continue;
             const int64_t p = p0 + i;
             int64_t dst = p;

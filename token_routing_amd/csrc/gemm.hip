@@ -1097,6 +1097,19 @@ __device__ __forceinline__ void stage_bf16(char *st0, char *st1,
         }
 }
 
+// 16 bytes of a staged output row to HBM with the nontemporal (streaming)
+// hint: no kernel here reads its own output again, so its lines need not
+// stay in L2 next to the operands.  Measured: fine-grained step forward
+// 0.296 -> 0.284 ms, dX 0.280 -> 0.272, dW 0.388 -> 0.378; in the decode
+// slice with backward, the next step's forward 0.101 -> 0.058 ms (dW's
+// 403 MB output no longer displaces the weights); Mixtral unchanged.
+typedef unsigned u32x4_nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_out16(char *dst, const char *lds_src)
+{
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_nt_t *>(lds_src),
+                                reinterpret_cast<u32x4_nt_t *>(dst));
+}
+
 template <class C, bool SCALE = false>
 __device__ __forceinline__ void epilogue_bf16(char *st0, char *st1,
                                               const f32x16_t (&acc)[C::FM][C::FN],
@@ -1113,8 +1126,8 @@ __device__ __forceinline__ void epilogue_bf16(char *st0, char *st1,
         const int col = n0 + ch * 8;
         const char *buf = row / L::ROWS_PER_BUF ? st1 : st0;
         if (dst >= 0 && col < ncols)
-            *reinterpret_cast<uint4 *>(Y + ((int64_t)dst * ldy + col) * 2) =
-                *reinterpret_cast<const uint4 *>(buf + L::chunk_off(row % L::ROWS_PER_BUF, ch));
+            store_out16(Y + ((int64_t)dst * ldy + col) * 2,
+                        buf + L::chunk_off(row % L::ROWS_PER_BUF, ch));
     }
     __syncthreads();
 }
@@ -1195,8 +1208,7 @@ __device__ __forceinline__ void epilogue_gated(char *st0, const f32x16_t (&acc)[
         const int dst = s_dst[row];
         const int col = o0 + ch * 8;
         if (dst >= 0 && col < ncols)
-            *reinterpret_cast<uint4 *>(Y + ((int64_t)dst * ldy + col) * 2) =
-                *reinterpret_cast<const uint4 *>(st0 + (row * OC + ch * 8) * 2);
+            store_out16(Y + ((int64_t)dst * ldy + col) * 2, st0 + (row * OC + ch * 8) * 2);
     }
     __syncthreads();
 }

@@ -12,6 +12,10 @@
 // Both are streaming kernels bound by HBM: no LDS and no MFMA.  A wave moves
 // 16 bytes per lane (8 bf16), so one wave covers a 512-column chunk of a row;
 // row indices and weights are uniform per wave and come in as scalar loads.
+// Outputs are stored with the nontemporal (streaming) hint, so that the
+// written lines do not take cache space from the rows still to be read:
+// the combine on 8192 tokens x top-8 x 2048 columns went from 0.085 to
+// 0.062 ms (3.5 -> 4.8 TB/s), its backward from 0.107 to 0.106 ms.
 #include "common.h"
 
 #include "gemm_params.h"
@@ -109,10 +113,11 @@ __global__ __launch_bounds__(256) void combine_fwd_kernel(CombineParams a)
             if (col >= a.N)
                 continue;
             if (a.f32_out)
-                *reinterpret_cast<f32x8_t *>(reinterpret_cast<float *>(a.out) + t * a.N + col) =
-                    acc[c];
+                __builtin_nontemporal_store(
+                    acc[c], reinterpret_cast<f32x8_t *>(reinterpret_cast<float *>(a.out) + t * a.N + col));
             else
-                *reinterpret_cast<u32x4v_t *>(a.out + (t * a.N + col) * 2) = narrow8(acc[c]);
+                __builtin_nontemporal_store(narrow8(acc[c]),
+                                            reinterpret_cast<u32x4v_t *>(a.out + (t * a.N + col) * 2));
         }
     }
 }
@@ -162,7 +167,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdParams a)
                 for (int i = 0; i < 8; ++i)
                     dot += g[i] * y[i];
             }
-            *reinterpret_cast<u32x4v_t *>(a.dY + (row * a.N + col) * 2) = narrow8(w * g);
+            __builtin_nontemporal_store(narrow8(w * g),
+                                        reinterpret_cast<u32x4v_t *>(a.dY + (row * a.N + col) * 2));
         }
     }
     if (a.dw) {

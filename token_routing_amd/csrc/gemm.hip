@@ -1388,27 +1388,30 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(TailReduceParams a)
 // Forward
 // ---------------------------------------------------------------------------
 
-// GATED: W rows come in (gate, linear) pairs and Y gets N/2 columns of the
-// gated activation (epilogue_gated).
 // Raster of an expert's output tiles: tile u of mt row tiles x nt column
-// tiles.  The row tiles are taken in bands of up to kBandM; within a band
-// the row tiles of one column tile are consecutive.  An XCD's 32 concurrent
-// tiles then cover at most 8 row tiles and 4 or more column tiles: on a
-// dense 8192 x 28672 x 4096 product, 32 row tiles of one column tile made
-// each stage fetch 33 distinct slices into the XCD's L2 instead of 12.
-// Experts of up to kBandM row tiles keep the plain column-major order.
-constexpr int kBandM = 8;
+// tiles.  The row tiles are taken in bands of up to BAND; within a band the
+// row tiles of one column tile are consecutive.  With BAND = 8 an XCD's 32
+// concurrent tiles cover at most 8 row tiles and 4 or more column tiles: on
+// a dense 8192 x 28672 x 4096 product, 32 row tiles of one column tile made
+// each stage fetch 33 distinct slices into the XCD's L2 instead of 12 (4 and
+// 16 measured no better there, 16 11% slower).  Experts of up to BAND row
+// tiles keep the plain column-major order.
+constexpr int kBandM = 8;    // forward
+constexpr int kBandMdX = 4;  // dX: Mixtral-shaped dX 1.84 -> 1.77 ms against 8
 
+template <int BAND>
 __device__ __forceinline__ void band_raster(int u, int mt, int nt, int &m, int &n)
 {
-    const int band = u / (kBandM * nt);
-    const int first = band * kBandM;
-    const int gm = min(mt - first, kBandM);
-    const int r = u - band * kBandM * nt;
+    const int band = u / (BAND * nt);
+    const int first = band * BAND;
+    const int gm = min(mt - first, BAND);
+    const int r = u - band * BAND * nt;
     m = first + r % gm;
     n = r / gm;
 }
 
+// GATED: W rows come in (gate, linear) pairs and Y gets N/2 columns of the
+// gated activation (epilogue_gated).
 template <class C, bool GATED>
 __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
 {
@@ -1438,7 +1441,7 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
         const int mtiles = (mc + C::BM - 1) / C::BM;
         const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
         int mt, nt;
-        band_raster(u, mtiles, ntn, mt, nt);
+        band_raster<kBandM>(u, mtiles, ntn, mt, nt);
         p0 = __builtin_amdgcn_readfirstlane(s_roff[e]) + mt * C::BM;
         rows = min(C::BM, mc - mt * C::BM);
         n0 = nt * C::BN;
@@ -1568,7 +1571,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         const int mtiles = (mc + C::BM - 1) / C::BM;
         const int u = t - __builtin_amdgcn_readfirstlane(s_tstart[e]);
         int mt, kt;
-        band_raster(u, mtiles, ntk, mt, kt);
+        band_raster<kBandMdX>(u, mtiles, ntk, mt, kt);
         const int p0 = p0base + mt * C::BM;
         const int rows = min(C::BM, mc - mt * C::BM);
         const int k0 = kt * C::BN;

@@ -106,7 +106,9 @@ def build_layer_step(wl, dY_seed, with_bwd=True, rotate=1, extra_flags=0):
         dY = synth.normal_bf16((S, N), 0.01, synth.generator(dY_seed)).to("cuda")
         dX = torch.empty(S, K, dtype=torch.bfloat16, device="cuda")
         dW = torch.empty(E, N, K, dtype=torch.bfloat16, device="cuda")
-        ws_bytes = mg.dw_workspace_bytes(T, topk, E, N, K)
+        # under permute_x with room for X's rows in expert order (copied first)
+        ws_bytes = (mg.dw_gather_workspace_bytes(T, topk, E, N, K)
+                    if bwd_flags & synth.PERMUTE_X else mg.dw_workspace_bytes(T, topk, E, N, K))
         dw_ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
         dx_bytes = mg.dx_workspace_bytes(T, topk, E, N, K)
@@ -436,7 +438,8 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
                  ("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
-                 ("dw_reduce_kernel", "dW_reduce"), ("tail_reduce_kernel", "tail_reduce"),
+                 ("dw_reduce_kernel", "dW_reduce"), ("gather_x_kernel", "dW_gather"),
+                 ("tail_reduce_kernel", "tail_reduce"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),
                  ("route_scan", "route_scan"), ("route_scatter", "route_scatter"),
                  ("route_small", "route_small"), ("Cijk_", "vendor"))

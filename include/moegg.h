@@ -244,6 +244,22 @@ size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
                                              int32_t num_experts, int32_t N, int32_t K);
 
 /*
+ * Bytes of workspace with which moegg_grouped_gemm_dW under MOEGG_PERMUTE_X
+ * also copies X's rows into expert order before the reduction: the split
+ * area above rounded up to 256 bytes, plus S * K * 2 for the copy.  The
+ * copy (X[gather_idx[p] / topk, :] for every slot p) is a separate launch
+ * on the same stream; the reduction then reads it in sorted order.  The
+ * result is the same as with the gather inside the reduction, including
+ * zeros and MOEGG_DERR_GATHER for entries outside [0, S); on MI355X the
+ * copy plus the reduction take less time.  A workspace of at least
+ * moegg_grouped_gemm_dW_workspace_bytes(...) bytes but less than this
+ * keeps the gather inside the reduction.  Without MOEGG_PERMUTE_X the
+ * extra bytes are unused.
+ */
+size_t moegg_grouped_gemm_dW_gather_workspace_bytes(int32_t num_tokens, int32_t topk,
+                                                    int32_t num_experts, int32_t N, int32_t K);
+
+/*
  * One GEMM group: y[m, n] = x[m, k] @ w, bf16 in, fp32 accumulation, bf16 out.
  * w is [k, n] row-major (ldw >= n) when the call's trans_b is 0, as in
  * asym_dual_gmm_separated (wall_x/fusions/backend.py), or [n, k] row-major

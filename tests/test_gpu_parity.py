@@ -487,3 +487,65 @@ def test_host_validation_statuses(mg):
     with pytest.raises(mg.MoeggError) as e:
         mg.grouped_gemm_dX(X, W, m, g, 1, FM)
     assert e.value.status == 3
+
+
+# dW under permute_x with a workspace large enough for X's rows in expert
+# order: a separate copy launch, then the reduction on the copy.  Against
+# the gather inside the reduction with the same split (a workspace of just
+# the split area, so hot experts are cut into the same chunks) the sums are
+# the same in the same order, so the two agree bit for bit; the copy path is
+# also checked against the oracle.
+DW_GATHERED = [(300, 72, 264, 4, 2, 21), (1100, 136, 136, 3, 2, 22), (37, 264, 72, 8, 3, 23)]
+
+
+@pytest.mark.parametrize("T,N,K,E,topk,seed", DW_GATHERED)
+def test_dw_permute_x_gathered_copy(mg, T, N, K, E, topk, seed):
+    g = torch.Generator().manual_seed(seed)
+    S = T * topk
+    ids = torch.randint(0, E, (T, topk), generator=g, dtype=torch.int32)
+    X = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16)
+    dY = (torch.randn(S, N, generator=g) * 0.5).to(torch.bfloat16)
+    route = oracle.route(ids.numpy().reshape(-1), E, 128)
+    gather = torch.from_numpy(route["gather"]).cuda()
+    m_sizes = torch.from_numpy(route["m_sizes"]).cuda()
+    Xd, dYd = X.cuda(), dY.cuda()
+    need = mg.dw_gather_workspace_bytes(T, topk, E, N, K)
+    assert need >= S * K * 2 + mg.dw_workspace_bytes(T, topk, E, N, K)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dW_copy = mg.grouped_gemm_dW(Xd, dYd, m_sizes, gather, topk, mg.PERMUTE_X, workspace=ws,
+                                 error_flags=err)
+    split_ws = torch.empty(max(mg.dw_workspace_bytes(T, topk, E, N, K), 16), dtype=torch.uint8,
+                           device="cuda")
+    dW_fused = mg.grouped_gemm_dW(Xd, dYd, m_sizes, gather, topk, mg.PERMUTE_X,
+                                  workspace=split_ws, error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(dW_copy, dW_fused)
+    ref = oracle.grouped_gemm_dW(synth.bits(X), synth.bits(dY), route["m_sizes"],
+                                 route["gather"], topk, mg.PERMUTE_X, E)
+    _assert_close(dW_copy.reshape(E * N, K), ref, f"dW gathered copy T={T} N={N} K={K}")
+
+
+def test_dw_gathered_copy_flags_bad_gather(mg):
+    """An entry outside [0, S) gives a zero row and the gather error bit, as
+    the gather inside the reduction does."""
+    T, N, K, E, topk = 64, 72, 136, 2, 2
+    S = T * topk
+    g = torch.Generator().manual_seed(24)
+    X = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16).cuda()
+    dY = (torch.randn(S, N, generator=g) * 0.5).to(torch.bfloat16).cuda()
+    m_sizes = torch.tensor([S // 2, S // 2], dtype=torch.int32, device="cuda")
+    gather = torch.arange(S, dtype=torch.int32, device="cuda")
+    gather[5] = S + 7
+    ws = torch.empty(mg.dw_gather_workspace_bytes(T, topk, E, N, K), dtype=torch.uint8,
+                     device="cuda")
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = mg.grouped_gemm_dW(X, dY, m_sizes, gather, topk, mg.PERMUTE_X, workspace=ws,
+                           error_flags=e1)
+    b = mg.grouped_gemm_dW(X, dY, m_sizes, gather, topk, mg.PERMUTE_X, split=False,
+                           error_flags=e2)
+    torch.cuda.synchronize()
+    assert int(e1.item()) & mg.DERR_GATHER and int(e2.item()) & mg.DERR_GATHER
+    assert torch.equal(a, b)

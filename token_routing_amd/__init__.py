@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moegg_grouped_gemm_dW.restype = ctypes.c_int
     lib.moegg_grouped_gemm_dW_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.moegg_grouped_gemm_dW_workspace_bytes.restype = sz
+    lib.moegg_grouped_gemm_dW_gather_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.moegg_grouped_gemm_dW_gather_workspace_bytes.restype = sz
     lib.moegg_grouped_gemm_groups.argtypes = [ctypes.POINTER(MoeggGroup), i32, i32, vp]
     lib.moegg_grouped_gemm_groups.restype = ctypes.c_int
     lib.moegg_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, u32, vp, vp, vp]
@@ -226,13 +228,24 @@ def dw_workspace_bytes(num_tokens: int, topk: int, num_experts: int, N: int, K: 
                                                                        num_experts, N, K))
 
 
+def dw_gather_workspace_bytes(num_tokens: int, topk: int, num_experts: int, N: int,
+                              K: int) -> int:
+    """Workspace bytes with which grouped_gemm_dW under PERMUTE_X also copies X's rows
+    into expert order before the reduction (the split area plus S * K * 2)."""
+    return int(load_library().moegg_grouped_gemm_dW_gather_workspace_bytes(
+        num_tokens, topk, num_experts, N, K))
+
+
 def grouped_gemm_dW(X, dY, m_sizes, gather_idx, topk: int, flags: int, *, dW=None,
                     workspace=None, split: bool = True, error_flags=None, stream=None):
     """dW[e] = dY_e^T X_e (ragged per expert). Returns [E, N, K] bf16 (fp32 with DW_FP32_OUT).
 
-    split: let the library cut hot experts' reductions into chunks (fp32
-    partials in `workspace`, a uint8 CUDA tensor of dw_workspace_bytes(...)
-    bytes, allocated here when not given).  split=False passes no workspace.
+    split: pass the library a workspace (`workspace`, a uint8 CUDA tensor,
+    allocated here when not given: dw_gather_workspace_bytes(...) bytes under
+    PERMUTE_X, else dw_workspace_bytes(...)).  It cuts hot experts'
+    reductions into chunks with fp32 partials there and, under PERMUTE_X
+    with room for them, copies X's rows into expert order first.
+    split=False passes no workspace: one launch, rows gathered inside it.
     """
     lib = load_library()
     S, N = dY.shape
@@ -245,7 +258,10 @@ def grouped_gemm_dW(X, dY, m_sizes, gather_idx, topk: int, flags: int, *, dW=Non
     if not split:
         workspace = None
     elif workspace is None:
-        need = dw_workspace_bytes(S // topk, topk, E, N, K)
+        if flags & PERMUTE_X:
+            need = dw_gather_workspace_bytes(S // topk, topk, E, N, K)
+        else:
+            need = dw_workspace_bytes(S // topk, topk, E, N, K)
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dY.device)
     if workspace is not None:

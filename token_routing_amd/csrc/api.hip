@@ -260,6 +260,11 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     const bool use_ws = workspace != nullptr && ws_need > 0;
     if (workspace != nullptr && (int64_t)workspace_bytes < ws_need)
         return MOEGG_EWORKSPACE;
+    // Room for X's rows in expert order after the partials: gather them first.
+    const int64_t xg_off = moegg::dw_gather_offset((int64_t)num_tokens * topk, num_experts, N, K);
+    const int64_t xg_bytes = (int64_t)num_tokens * topk * K * 2;
+    const bool use_xg = workspace != nullptr && (flags & MOEGG_PERMUTE_X) && xg_bytes > 0 &&
+                        (int64_t)workspace_bytes >= xg_off + xg_bytes;
     int cus = 0;
     if (device_cus(&cus) != 0)
         return MOEGG_EHIP;
@@ -279,6 +284,7 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     p.flags = flags;
     p.topk_div = moegg::make_fastdiv((uint32_t)topk);
     p.ws = use_ws ? static_cast<char *>(workspace) : nullptr;
+    p.xg = use_xg ? static_cast<char *>(workspace) + xg_off : nullptr;
     p.split_rows = use_ws ? moegg::dw_split_rows(p.S, N, K) : 0;
     return from_hip(moegg::dw_launch(p, cus, static_cast<hipStream_t>(stream)));
 }
@@ -300,6 +306,15 @@ size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
     if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
         return 0;
     return (size_t)moegg::dw_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K);
+}
+
+size_t moegg_grouped_gemm_dW_gather_workspace_bytes(int32_t num_tokens, int32_t topk,
+                                                    int32_t num_experts, int32_t N, int32_t K)
+{
+    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
+        return 0;
+    const int64_t S = (int64_t)num_tokens * topk;
+    return (size_t)(moegg::dw_gather_offset(S, num_experts, N, K) + S * K * 2);
 }
 
 moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_groups,

@@ -2350,6 +2350,38 @@ int64_t dw_workspace_bytes(int64_t S, int E, int N, int K)
     return dw_header_bytes(E) + partials * N * K * 4;
 }
 
+// Byte offset of the gathered X rows in dW's workspace, after the split
+// partials.
+int64_t dw_gather_offset(int64_t S, int E, int N, int K)
+{
+    return (dw_workspace_bytes(S, E, N, K) + 255) / 256 * 256;
+}
+
+// X rows in expert order for dW under permute_x, when the caller's
+// workspace has room for them: xg[p, :] = X[gather[p] / topk, :].  The
+// reduction then reads xg in sorted order.  On the Mixtral shape (8192 slots,
+// K 4096) the copy takes 0.020 ms and dW 2.00-2.05 ms, against 2.17-2.20 ms
+// for the row gather inside dW, with the same result bit for bit: the
+// scattered row reads cost dW's copy path more than one streaming pass
+// costs.  One workgroup per row at a time; an entry outside [0, S) gives a
+// zero row and is reported, as the gather inside dW does.  Plain stores:
+// dW reads the copy right after.
+__global__ __launch_bounds__(256) void gather_x_kernel(DwParams a)
+{
+    const int cpr = a.K / 8;  // 16-byte chunks per row
+    for (int64_t p = blockIdx.x; p < a.S; p += gridDim.x) {
+        const int g = __builtin_amdgcn_readfirstlane(a.gather[p]);
+        const bool ok = g >= 0 && g < a.S;
+        if (!ok && threadIdx.x == 0)
+            raise_error(a.err, kErrGather);
+        const char *src = a.X + (int64_t)(ok ? g / a.topk : 0) * a.K * 2;
+        char *dst = a.xg + p * a.K * 2;
+        for (int c = threadIdx.x; c < cpr; c += blockDim.x)
+            *reinterpret_cast<uint4 *>(dst + c * 16) =
+                ok ? *reinterpret_cast<const uint4 *>(src + c * 16) : uint4{0, 0, 0, 0};
+    }
+}
+
 template <bool PX, bool PY>
 static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 {
@@ -2366,8 +2398,15 @@ static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 }
 
 
-hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream)
+hipError_t dw_launch(const DwParams &pin, int cus, hipStream_t stream)
 {
+    DwParams p = pin;
+    if (p.xg && (p.flags & MOEGG_PERMUTE_X) && p.S > 0) {
+        hipLaunchKernelGGL(gather_x_kernel, dim3((unsigned)std::min<int64_t>(p.S, (int64_t)cus * 16)),
+                           dim3(256), 0, stream, p);
+        p.X = p.xg;
+        p.flags &= ~MOEGG_PERMUTE_X;
+    }
     if (p.flags & MOEGG_PERMUTE_X)
         dw_launch_flags<true, false>(p, cus, stream);
     else if (p.flags & MOEGG_PERMUTE_Y)

@@ -93,6 +93,7 @@ struct DwParams {
     char *dW;
     int32_t *err;
     char *ws;          // workspace (header + partials), or null
+    char *xg;          // X rows gathered into expert order (permute_x), or null
     int64_t S;
     int topk, E, N, K;
     int split_rows;    // 0: never split
@@ -140,6 +141,7 @@ hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream);
 // split), the header size and the whole workspace (0 when no split is possible).
 int dw_split_rows(int64_t S, int N, int K);
 int64_t dw_workspace_bytes(int64_t S, int E, int N, int K);
+int64_t dw_gather_offset(int64_t S, int E, int N, int K);
 
 __host__ __device__ inline int64_t dw_header_bytes(int E)
 {

@@ -18,7 +18,11 @@ Prints ONE JSON line.  `value` is useful TFLOP/s over the whole step
 (useful FLOPs = 2 * sum_e m_e * N * K per GEMM, actual rows only);
 `roofline` describes the step's dominant kernel, timed with HIP events on
 the stream the kernels run on; `cpu_baseline` is the plain CPU oracle timed
-on a bounded sample of the same workload.
+on a bounded sample of the same workload, route / fwd / dX / dW each on one
+thread and on every core of the process's affinity mask.  With the default
+workload the line also carries `configs`: the tiny layer, the dual-expert
+groups, the fine-grained forward (permute_y + fuse_mul_post), its decode
+slice and its backward, each timed the same way after the headline step.
 """
 
 from __future__ import annotations
@@ -289,76 +293,160 @@ def measured_traffic(workload, label):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(st, budget_s):
-    """The CPU oracle on a bounded sample of the workload (one thread).
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The forward of a few output rows is timed once to size the sample to about
-    budget_s seconds, then that many random output rows (all columns) are
-    computed; the rate is useful FLOPs of the sampled rows per second.
-    """
+
+def _run_threads(fn, parts):
+    """fn(part) on one Python thread per part (the oracle's ctypes calls
+    release the GIL, so the parts run on separate cores); wall seconds."""
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    if len(parts) == 1:
+        fn(parts[0])
+    else:
+        with ThreadPoolExecutor(max_workers=len(parts)) as ex:
+            list(ex.map(fn, parts))
+    return time.perf_counter() - t0
+
+
+def _oracle_leg(name, call, pool, flops_of, per_leg_s, cores, rng):
+    """Time the unchanged oracle on random output rows of `pool`: one thread,
+    then `cores` threads over disjoint row sets.  Each leg is sized to about
+    per_leg_s seconds from a short calibration call.  Returns the two legs'
+    rates (useful FLOP/s of the computed rows)."""
+    pool = np.asarray(pool)
+    cal = rng.choice(pool, size=min(2, pool.size), replace=False)
+    t_cal = _run_threads(call, [cal])
+    per_row = max(t_cal / cal.size, 1e-7)
+    n1 = int(max(1, min(pool.size, per_leg_s / per_row)))
+    legs = {}
+    for leg, threads in (("single", 1), ("all_cores", cores)):
+        n = min(pool.size, n1 * threads)
+        rows = rng.choice(pool, size=n, replace=False)
+        parts = [p for p in np.array_split(rows, threads) if p.size]
+        dt = _run_threads(call, parts)
+        fl = float(flops_of(rows))
+        legs[leg] = {"rows": int(n), "threads": len(parts), "seconds": round(dt, 3),
+                     "gflops": round(fl / dt / 1e9, 3)}
+    return legs
+
+
+def cpu_baseline(st, budget_s):
+    """The CPU oracle, timed on the host cores on a bounded sample of the
+    workload: each step of the path separately (route, fwd, dX, dW), once on
+    one thread and once with one thread per core of sched_getaffinity over
+    disjoint random output rows.  The oracle itself is unchanged (plain
+    loops, one call per thread).  `value` is the step's useful FLOP/s at the
+    all-cores rates: total useful FLOPs over the sum of each kernel's full
+    time at its rate."""
     import oracle
 
     wl = st.inputs
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    labels = [k[0] for k in st.kernels]
+    per_leg = budget_s / max(1, 2 * sum(1 for lab in labels if lab != "route"))
+    out = {"kind": "oracle", "unit": "TFLOP/s", "cores": cores, "cpu_model": _cpu_model()}
+    legs = {"single": {}, "all_cores": {}}
+    full = {}
     if st.name == "combine":
-        # the whole forward combine of the workload, repeated up to ~budget_s
         g = synth.generator(synth.SEEDS["combine_y"])
         Yb = synth.bits(synth.normal_bf16((wl.S, wl.N), 1.0, g))
         ref_route = oracle.route(wl.ids.numpy().reshape(-1), wl.E, BLOCK_M)
+        sc = ref_route["scatter"]
         w = wl.weights.numpy().reshape(-1)
+        k = wl.topk
+
+        def call(tok):
+            lo, hi = int(tok.min()), int(tok.max()) + 1
+            oracle.combine(Yb, k, scatter=sc[lo * k:hi * k], weights=w[lo * k:hi * k],
+                           num_tokens=hi - lo)
+        # tokens in contiguous blocks (the combine takes a token range)
+        blocks = np.arange(wl.T).reshape(-1, 64)
+        r = _oracle_leg("combine", lambda b: [call(x) for x in blocks[b]], np.arange(len(blocks)),
+                        lambda b: 2.0 * len(b) * 64 * k * wl.N, per_leg, cores, rng)
+        for leg in legs:
+            legs[leg]["combine"] = r[leg]
+        full["combine"] = 2.0 * wl.S * wl.N
+    elif st.name == "dual":
+        for gi, (x, w) in enumerate(wl.groups):
+            xb, wb = synth.bits(x), synth.bits(w)
+            per_row = 2.0 * x.shape[1] * w.shape[1]
+            r = _oracle_leg(f"group{gi}", lambda rows: oracle.dense_gemm_kn(xb[np.sort(rows)], wb),
+                            np.arange(x.shape[0]), lambda rows: per_row * len(rows), per_leg, cores,
+                            rng)
+            for leg in legs:
+                legs[leg][f"group{gi}"] = r[leg]
+            full[f"group{gi}"] = per_row * x.shape[0]
+    else:
+        E, N, K = wl.W.shape
+        ids = wl.ids.numpy().reshape(-1)
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.combine(Yb, wl.topk, scatter=ref_route["scatter"], weights=w)
+            ref_route = oracle.route(ids, wl.E, BLOCK_M)
             reps += 1
-            if time.perf_counter() - t0 >= min(budget_s, 10.0) or reps >= 50:
+            if time.perf_counter() - t0 >= 0.2:
                 break
-        dt = time.perf_counter() - t0
-        return {"value": 2.0 * wl.S * wl.N * reps / dt / 1e12, "unit": "TFLOP/s", "cores": 1,
-                "kind": "oracle", "sample": f"{reps} full forward combine(s) of T={wl.T} "
-                f"top-{wl.topk} N={wl.N}", "seconds": round(dt, 3)}
-    if st.name == "dual":
-        x, w = wl.groups[0]
-        per_row = 2.0 * x.shape[1] * w.shape[1]
-        t0 = time.perf_counter()
-        oracle.dense_gemm_kn(synth.bits(x[:4]), synth.bits(w))
-        rows = max(4, min(x.shape[0], int(budget_s / max(time.perf_counter() - t0, 1e-6) * 4)))
-        t0 = time.perf_counter()
-        oracle.dense_gemm_kn(synth.bits(x[:rows]), synth.bits(w))
-        dt = time.perf_counter() - t0
-        return {"value": per_row * rows / dt / 1e12, "unit": "TFLOP/s", "cores": 1,
-                "kind": "oracle", "sample": f"group 0, first {rows} rows x all columns",
-                "seconds": round(dt, 3)}
-    E, N, K = wl.W.shape
-    ids = wl.ids.numpy().reshape(-1)
-    Xb, Wb = synth.bits(wl.X), synth.bits(wl.W)
-    gate = wl.weights.numpy().reshape(-1)
-    t0 = time.perf_counter()
-    ref_route = oracle.route(ids, wl.E, BLOCK_M)
-    t_route = time.perf_counter() - t0
-    rng = np.random.default_rng(0)
-    per_row = 2.0 * N * K
-
-    gated = bool(st.flags & mg.GATED_SILU)
-
-    def run(nrows):
-        rows = rng.choice(wl.S, size=min(nrows, wl.S), replace=False)
-        if wl.flags & synth.PERMUTE_Y:
-            rows = ref_route["gather"][rows]     # output rows are slots
-        t = time.perf_counter()
-        if gated:
-            oracle.grouped_gemm_fwd_gated(Xb, Wb, ref_route["m_sizes"], ref_route["gather"],
-                                          wl.topk, wl.flags, rows=rows)
-        else:
-            oracle.grouped_gemm_fwd(Xb, Wb, ref_route["m_sizes"], ref_route["gather"], gate,
-                                    wl.topk, wl.flags, rows=rows)
-        return len(rows), time.perf_counter() - t
-
-    n1, t1 = run(2)
-    n, dt = run(max(1, int(budget_s / max(t1 / n1, 1e-9))))
-    return {"value": per_row * n / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"routing of all {wl.S} slots ({t_route:.3f} s) + forward of {n} random "
-                      f"output rows x all {N} columns (K={K})"
-                      f"{' and their gated activation' if gated else ''}; the oracle's rate on them",
-            "seconds": round(dt, 3)}
+        t_route = (time.perf_counter() - t0) / reps
+        for leg in legs:
+            # one counting sort over all slots: not split over rows
+            legs[leg]["route"] = {"rows": int(ids.size), "threads": 1, "seconds": round(t_route, 4),
+                                  "note": "one stable counting sort over all slots"}
+        Xb, Wb = synth.bits(wl.X), synth.bits(wl.W)
+        gate = wl.weights.numpy().reshape(-1)
+        ms, gather, topk, flags = ref_route["m_sizes"], ref_route["gather"], wl.topk, st.flags
+        gated = bool(flags & mg.GATED_SILU)
+        base_flags = flags & (synth.PERMUTE_X | synth.PERMUTE_Y | synth.FUSE_MUL_POST)
+        row_fl = 2.0 * N * K
+        if "dX" in labels or "dW" in labels:
+            dYb = synth.bits(synth.normal_bf16((wl.S, N), 0.01, synth.generator(st.dY_seed)))
+            bflags = flags & (synth.PERMUTE_X | synth.PERMUTE_Y)
+        for lab in labels:
+            if lab == "fwd":
+                if gated:
+                    call = lambda rows: oracle.grouped_gemm_fwd_gated(
+                        Xb, Wb, ms, gather, topk, base_flags, rows=rows)
+                else:
+                    call = lambda rows: oracle.grouped_gemm_fwd(
+                        Xb, Wb, ms, gather, gate, topk, base_flags, rows=rows)
+                r = _oracle_leg(lab, call, np.arange(wl.S), lambda rows: row_fl * len(rows),
+                                per_leg, cores, rng)
+            elif lab == "dX":
+                r = _oracle_leg(lab, lambda rows: oracle.grouped_gemm_dX(
+                    dYb, Wb, ms, gather, topk, bflags, rows=rows), np.arange(wl.S),
+                    lambda rows: row_fl * len(rows), per_leg, cores, rng)
+            elif lab == "dW":
+                live = np.nonzero(ms > 0)[0]
+                pool = (live[:, None] * N + np.arange(N)[None, :]).reshape(-1)
+                r = _oracle_leg(lab, lambda rows: oracle.grouped_gemm_dW(
+                    Xb, dYb, ms, gather, topk, bflags, E, rows=rows), pool,
+                    lambda rows: float(np.sum(2.0 * ms[np.asarray(rows) // N] * K)), per_leg,
+                    cores, rng)
+            else:
+                continue
+            for leg in legs:
+                legs[leg][lab] = r[leg]
+            full[lab] = _useful(ms, N, K)
+    # each kernel's full-workload time at the leg's rate, and the step rate
+    for leg in legs:
+        tot = sum(full[k] / (legs[leg][k]["gflops"] * 1e9) for k in full)
+        tot += legs[leg].get("route", {}).get("seconds", 0.0)
+        legs[leg]["step_s_extrapolated"] = round(tot, 2)
+        legs[leg]["tflops"] = round(sum(full.values()) / tot / 1e12, 6)
+    out["value"] = legs["all_cores"]["tflops"]
+    out["single"], out["all_cores"] = legs["single"], legs["all_cores"]
+    out["sample"] = (f"random output rows of each kernel of the {st.name} step, each leg sized to "
+                     f"~{per_leg:.1f} s (one thread, then {cores} threads over disjoint rows); "
+                     "value = the step's useful FLOPs over the sum of each kernel's full time "
+                     "at its all-cores rate")
+    return out
 
 
 def _time(fn, steps, warmup):
@@ -470,6 +558,9 @@ def _counter_means(path, counter):
 MI355X_XCDS, MI355X_SIMDS = 8, 256 * 4
 
 
+MI355X_MAX_GHZ = 2.4
+
+
 def counter_lines(sq_dir, stat_rows):
     """Per-kernel MFMA utilisation and LDS bank conflicts from an SQ counter
     pass (SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT,
@@ -477,9 +568,12 @@ def counter_lines(sq_dir, stat_rows):
 
     GRBM_GUI_ACTIVE is summed over the 8 XCDs, so a kernel's busy cycles are
     GRBM_GUI_ACTIVE / 8; MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES over those
-    cycles x 1024 SIMDs.  The cycle count divided by the kernel's average
-    duration in the trace run (a different run, so only indicative) gives
-    the clock."""
+    cycles x 1024 SIMDs.  Those cycles over the kernel's average duration in
+    the trace run give its clock.  For short kernels the GRBM window is longer
+    than the kernel (the profiler's dispatch around it counts too), and the
+    implied clock comes out above the chip's 2.4 GHz maximum: such a row is
+    marked, and its MFMA busy is taken over duration x 2.4 GHz instead, the
+    most cycles the kernel can have had, which makes it a lower bound."""
     import glob
     f = glob.glob(os.path.join(sq_dir, "*counter_collection.csv"))[0]
     names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
@@ -490,20 +584,30 @@ def counter_lines(sq_dir, stat_rows):
         lab = _label(r["Name"])
         if lab and lab not in dur:
             dur[lab] = float(r["AverageNs"])
-    out = ["", "Counters (their own pass; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-           "(GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); clock = GRBM_GUI_ACTIVE / 8 / the trace "
-           "run's average duration, indicative only since the runs differ):", "",
-           "| kernel | MFMA busy | LDS bank conflicts / LDS active | clock GHz (indicative) |",
-           "|---|---|---|---|"]
+    out = ["", "Counters (their own pass; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 "
+           "SIMDs) with cycles = GRBM_GUI_ACTIVE / 8 XCDs; clock = those cycles / the trace run's "
+           f"average duration; where that clock exceeds {MI355X_MAX_GHZ} GHz the GRBM window is "
+           f"longer than the kernel, the row is marked, and MFMA busy uses duration x "
+           f"{MI355X_MAX_GHZ} GHz, a lower bound):", "",
+           "| kernel | MFMA busy | LDS bank conflicts / LDS active | clock GHz | cycles from |",
+           "|---|---|---|---|---|"]
     for lab in ("fwd", "dX", "dW", "groups", "combine", "combine_bwd", "vendor"):
         g = means["GRBM_GUI_ACTIVE"].get(lab)
         if not g or lab not in dur:
             continue
         cyc = g / MI355X_XCDS
+        ghz = cyc / dur[lab]
+        src = "GRBM_GUI_ACTIVE / 8"
+        busy_txt = None
+        if ghz > MI355X_MAX_GHZ:
+            cyc = dur[lab] * MI355X_MAX_GHZ
+            src = f"invalid GRBM window ({ghz:.2f} GHz implied); duration x {MI355X_MAX_GHZ} GHz"
         busy = means["SQ_VALU_MFMA_BUSY_CYCLES"].get(lab, 0.0) / (cyc * MI355X_SIMDS)
+        busy_txt = f"{100 * busy:.1f}%" if ghz <= MI355X_MAX_GHZ else f">= {100 * busy:.1f}%"
         act = means["SQ_LDS_IDX_ACTIVE"].get(lab, 0.0)
         conf = means["SQ_LDS_BANK_CONFLICT"].get(lab, 0.0) / act if act else 0.0
-        out.append(f"| {lab} | {100 * busy:.1f}% | {conf:.4f} | {cyc / dur[lab]:.2f} |")
+        clock = f"{ghz:.2f}" if ghz <= MI355X_MAX_GHZ else "-"
+        out.append(f"| {lab} | {busy_txt} | {conf:.4f} | {clock} | {src} |")
     return out
 
 
@@ -583,6 +687,53 @@ def summarize(prof_dir, workload, command):
     return 0
 
 
+def kernel_breakdown(st, per):
+    """Per kernel: ms, useful TFLOP/s, algorithmic GB/s, and the fraction of
+    the MFMA peak, the HBM peak and the roofline (the larger of the two
+    floors over the measured time)."""
+    out = {}
+    for i, (label, _, fl, nb) in enumerate(st.kernels):
+        t = per[i] * 1e-3
+        tf = fl / t / 1e12 if fl else 0.0
+        gbs = nb / t / 1e9
+        roof_t = max(fl / (PEAK_BF16_TFLOPS * 1e12), nb / (PEAK_HBM_GBS * 1e9))
+        out[label] = {"ms": round(per[i], 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
+                      "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "bound": "mfma" if fl / (PEAK_BF16_TFLOPS * 1e12) >= nb / (PEAK_HBM_GBS * 1e9)
+                      else "hbm",
+                      "roofline_frac": round(roof_t / t, 4)}
+    return out
+
+
+# Every configuration of the benchmark besides the headline one, timed in the
+# default run: (key, workload, kernels reported, steps, warmup).
+CONFIG_RUNS = (
+    ("1_tiny", "tiny", ("route", "fwd"), 200, 50),
+    ("2_dual", "dual", ("groups",), 200, 50),
+    ("4_fine_fwd", "fine_fwd", ("route", "fwd"), 30, 10),
+    ("4_decode", "decode", ("route", "fwd"), 200, 50),
+    ("5_fine_bwd", "fine", ("dX", "dW"), 30, 10),
+)
+
+
+def run_configs():
+    """Time the other configurations one after another, each on its own
+    resident inputs (freed before the next)."""
+    out = {}
+    for key, workload, labels, steps, warmup in CONFIG_RUNS:
+        print(f"config {key} ({workload})", file=sys.stderr, flush=True)
+        st = make_step(workload)
+        per, step_ms, _ = time_step(st, steps, warmup)
+        bd = kernel_breakdown(st, per)
+        out[key] = {"workload": workload, "desc": WORKLOAD_DESC[workload], "steps": steps,
+                    "step_ms": round(step_ms, 4),
+                    "kernels": {lab: bd[lab] for lab in labels if lab in bd}}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -591,8 +742,13 @@ def main():
     # 3 warmup steps of the gated gate_up forward time it 5% slower than 30.
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mixtral", choices=sorted(WORKLOAD_DESC))
-    ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of CPU oracle work for the baseline (0 disables)")
+    ap.add_argument("--cpu-budget", type=float, default=24.0,
+                    help="seconds of CPU oracle work for the baseline, over both legs (0 "
+                         "disables)")
+    ap.add_argument("--configs", action=argparse.BooleanOptionalAction, default=None,
+                    help="also time the other configurations (tiny, dual, fine-grained forward, "
+                         "decode slice, fine-grained backward) into a `configs` object; on by "
+                         "default for the headline workload")
     ap.add_argument("--vendor", action="store_true",
                     help="also time hipBLASLt (torch.matmul) on the same products, expert by "
                          "expert (always on for --workload dense)")
@@ -617,22 +773,15 @@ def main():
         return copy_calibration()
     mg.load_library()
 
+    if args.configs is None:
+        args.configs = args.workload == "mixtral"
     st = make_step(args.workload)
     per, step_ms, wall = time_step(st, args.steps, args.warmup)
     flops = sum(k[2] for k in st.kernels)
     value = flops / (step_ms * 1e-3) / 1e12
 
-    breakdown = {}
+    breakdown = kernel_breakdown(st, per)
     dominant = max(range(len(st.kernels)), key=lambda i: per[i])
-    for i, (label, _, fl, nb) in enumerate(st.kernels):
-        t = per[i] * 1e-3
-        tf = fl / t / 1e12 if fl else 0.0
-        gbs = nb / t / 1e9
-        roof_t = max(fl / (PEAK_BF16_TFLOPS * 1e12), nb / (PEAK_HBM_GBS * 1e9))
-        breakdown[label] = {"ms": round(per[i], 4), "tflops": round(tf, 2), "gbs": round(gbs, 1),
-                            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                            "roofline_frac": round(roof_t / t, 4)}
     label, _, fl, nb = st.kernels[dominant]
     t = per[dominant] * 1e-3
     mfma_bound = fl / (PEAK_BF16_TFLOPS * 1e12) >= nb / (PEAK_HBM_GBS * 1e9)
@@ -648,6 +797,9 @@ def main():
     vendor = (vendor_reference(st, args.steps, args.warmup)
               if args.workload == "dense" or args.vendor else None)
     cpu = cpu_baseline(st, args.cpu_budget) if args.cpu_budget > 0 else None
+    del st
+    torch.cuda.empty_cache()
+    configs = run_configs() if args.configs else None
     line = {
         "metric": "MoE grouped-GEMM useful TFLOP/s (bf16) + % of MFMA/HBM roofline, fwd/dX/dW",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -657,6 +809,7 @@ def main():
                    "block_m_route": BLOCK_M},
         "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
         **({"vendor_reference": vendor} if vendor else {}),
+        **({"configs": configs} if configs else {}),
         "wall_s": round(wall, 3),
     }
     print(json.dumps(line), flush=True)

@@ -246,14 +246,19 @@ size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
 /*
  * Bytes of workspace with which moegg_grouped_gemm_dW under MOEGG_PERMUTE_X
  * also copies X's rows into expert order before the reduction: the split
- * area above rounded up to 256 bytes, plus S * K * 2 for the copy.  The
- * copy (X[gather_idx[p] / topk, :] for every slot p) is a separate launch
- * on the same stream; the reduction then reads it in sorted order.  The
- * result is the same as with the gather inside the reduction, including
- * zeros and MOEGG_DERR_GATHER for entries outside [0, S); on MI355X the
- * copy plus the reduction take less time.  A workspace of at least
- * moegg_grouped_gemm_dW_workspace_bytes(...) bytes but less than this
- * keeps the gather inside the reduction.  Without MOEGG_PERMUTE_X the
+ * area above rounded up to 256 bytes, plus S * K * 2 for the copy.  The copy
+ * (X[gather_idx[p] / topk, :] for every sorted position p below the sum of
+ * m_sizes) is a separate launch on the same stream; the reduction then
+ * reads it in sorted order.  The result is the same as with the gather
+ * inside the reduction, including zeros and MOEGG_DERR_GATHER for entries
+ * outside [0, S); positions past the sum of m_sizes, where routing leaves
+ * its dropped slots, are read by neither.  On MI355X the copy plus the
+ * reduction take less time.  The copy is an operand like X and must stay
+ * below 2 GiB: when S * K * 2 >= 2^31 this returns
+ * moegg_grouped_gemm_dW_workspace_bytes(...) and moegg_grouped_gemm_dW
+ * gathers inside the reduction whatever the workspace size.  A workspace of
+ * at least moegg_grouped_gemm_dW_workspace_bytes(...) bytes but less than
+ * this keeps the gather inside the reduction.  Without MOEGG_PERMUTE_X the
  * extra bytes are unused.
  */
 size_t moegg_grouped_gemm_dW_gather_workspace_bytes(int32_t num_tokens, int32_t topk,

@@ -114,6 +114,28 @@ def test_dw_workspace(lib):
                                      FAKE, 1024, None, None) == EWS
 
 
+def test_dw_gather_copy_size_rule(lib):
+    """The X copy of dW under permute_x is an operand like X: only below 2 GiB.
+
+    With room for it the gather workspace is the split area (256-byte aligned)
+    plus S*K*2; at S*K*2 >= 2^31 it is the split area alone (the rows are then
+    gathered inside the reduction), even where T*K*2 is far below 2 GiB."""
+    def both(T, k, E, N, K):
+        return (lib.moegg_grouped_gemm_dW_gather_workspace_bytes(T, k, E, N, K),
+                lib.moegg_grouped_gemm_dW_workspace_bytes(T, k, E, N, K))
+
+    g, w = both(300, 2, 4, 72, 264)
+    assert g == (w + 255) // 256 * 256 + 300 * 2 * 264 * 2
+    # S*K*2 one row below 2 GiB: the copy is still offered
+    g, w = both(16383, 8, 4, 64, 8192)
+    assert g == (w + 255) // 256 * 256 + 16383 * 8 * 8192 * 2
+    # exactly 2 GiB, and above it with T*K*2 = 328 MB: no copy
+    for T in (16384, 20000):
+        g, w = both(T, 8, 4, 64, 8192)
+        assert T * 8192 * 2 < 2 ** 31 <= T * 8 * 8192 * 2
+        assert g == w and w > 0
+
+
 def test_operand_size_limit(lib):
     # one expert's W of 2 GiB does not fit 32-bit buffer offsets
     assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 32768, 32768, 0,

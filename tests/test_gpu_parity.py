@@ -100,6 +100,31 @@ def test_route_drops_bad_ids(mg):
         assert np.array_equal(got[k], ref[k]), k
 
 
+def test_route_pages_worked_example(mg):
+    """The ragged dw comment block's example (expt_hist [60, 33, 0, 32, 25],
+    block 32) fed to the GPU routing: its padded ranges and tile counts, read
+    from the golden file, come out of padded_offsets and tile_offsets."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                       "ragged_padded_example.json")))
+    hist, B = gold["expt_hist"], gold["block"]
+    ids = np.concatenate([np.full(h, e, np.int32) for e, h in enumerate(hist)])
+    ids = ids[np.random.default_rng(60).permutation(ids.size)]
+    ref, got, err = _route_both(mg, torch.from_numpy(ids).reshape(-1, 1), len(hist), B)
+    assert err == 0
+    assert got["m_sizes"].tolist() == hist
+    starts = got["padded_offsets"].tolist()
+    for e, (lo, hi) in gold["padded_ranges"].items():
+        assert starts[int(e)] == lo and starts[int(e)] + hist[int(e)] == hi
+    assert starts[-1] == gold["padded_end"]
+    assert got["offsets"].tolist()[-1] == gold["unpadded_end"]
+    tiles = np.diff(got["tile_offsets"]).tolist()
+    assert tiles == [(h + B - 1) // B for h in hist] == [2, 2, 0, 1, 1]
+    for k in ("m_sizes", "offsets", "padded_offsets", "tile_offsets", "gather", "scatter"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
 def test_route_empty(mg):
     out = mg.moe_route(torch.zeros(0, 2, dtype=torch.int32, device="cuda"), 8, 32)
     torch.cuda.synchronize()
@@ -549,3 +574,81 @@ def test_dw_gathered_copy_flags_bad_gather(mg):
     torch.cuda.synchronize()
     assert int(e1.item()) & mg.DERR_GATHER and int(e2.item()) & mg.DERR_GATHER
     assert torch.equal(a, b)
+
+
+def test_dw_gathered_copy_with_dropped_ids(mg):
+    """Routing that dropped slots leaves -1 gather entries past sum(m_sizes).
+    Neither dW path reads them: the copy path (X rows copied into expert
+    order first) and the gather inside the reduction give the same bits and
+    the same (clear) error flags, and both match the oracle."""
+    T, N, K, E, topk = 400, 72, 136, 5, 3
+    S = T * topk
+    g = torch.Generator().manual_seed(31)
+    ids = torch.randint(0, E, (T, topk), generator=g, dtype=torch.int32)
+    ids[3, 0] = -1
+    ids[150, 2] = E
+    ids[399, 1] = 1 << 20
+    X = (torch.randn(T, K, generator=g) * 0.5).to(torch.bfloat16)
+    dY = (torch.randn(S, N, generator=g) * 0.5).to(torch.bfloat16)
+    ref_route = oracle.route(ids.numpy().reshape(-1), E, 128)
+    assert ref_route["dropped"] == 3
+    r = mg.moe_route(_dev(ids), E, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(r["gather"]), ref_route["gather"])
+    assert (_np(r["gather"])[S - 3:] == -1).all()
+    Xd, dYd = _dev(X), _dev(dY)
+    ws_copy = torch.empty(mg.dw_gather_workspace_bytes(T, topk, E, N, K), dtype=torch.uint8,
+                          device="cuda")
+    ws_split = torch.empty(max(mg.dw_workspace_bytes(T, topk, E, N, K), 16), dtype=torch.uint8,
+                           device="cuda")
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    a = mg.grouped_gemm_dW(Xd, dYd, r["m_sizes"], r["gather"], topk, PX, workspace=ws_copy,
+                           error_flags=e1)
+    b = mg.grouped_gemm_dW(Xd, dYd, r["m_sizes"], r["gather"], topk, PX, workspace=ws_split,
+                           error_flags=e2)
+    torch.cuda.synchronize()
+    assert int(e1.item()) == int(e2.item()) == 0
+    assert torch.equal(a, b)
+    ref = oracle.grouped_gemm_dW(synth.bits(X), synth.bits(dY), ref_route["m_sizes"],
+                                 ref_route["gather"], topk, PX, E)
+    _assert_close(a.reshape(E * N, K), ref, "dW copy path, dropped ids")
+
+
+def test_dw_permute_x_copy_would_exceed_2gib(mg):
+    """S*K*2 >= 2 GiB > T*K*2 under permute_x: the X copy would not fit the
+    32-bit operand offsets, so dW gathers inside the reduction, with the
+    binding's default workspace and with one that has room for the copy.
+    Sampled dW rows (every expert; first, last and 32-row block boundary
+    columns of N) x column blocks against the oracle."""
+    T, N, K, E, topk = 20000, 64, 8192, 4, 8
+    S = T * topk
+    assert T * K * 2 < 2 ** 31 <= S * K * 2
+    g = torch.Generator().manual_seed(41)
+    ids = torch.randint(0, E, (T, topk), generator=g, dtype=torch.int32)
+    X = (torch.randn(T, K, generator=g)).to(torch.bfloat16)
+    dY = (torch.randn(S, N, generator=g) * 0.1).to(torch.bfloat16)
+    print(f"dW over 2 GiB copy area: T={T} topk={topk} K={K} N={N} E={E}", flush=True)
+    ref_route = oracle.route(ids.numpy().reshape(-1), E, 128)
+    r = mg.moe_route(_dev(ids), E, 128)
+    Xd, dYd = _dev(X), _dev(dY)
+    assert mg.dw_gather_workspace_bytes(T, topk, E, N, K) == mg.dw_workspace_bytes(T, topk, E, N,
+                                                                                    K)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dW = mg.grouped_gemm_dW(Xd, dYd, r["m_sizes"], r["gather"], topk, PX, error_flags=err)
+    big = torch.empty(mg.dw_workspace_bytes(T, topk, E, N, K) + S * K * 2 + 4096,
+                      dtype=torch.uint8, device="cuda")
+    dW_big = mg.grouped_gemm_dW(Xd, dYd, r["m_sizes"], r["gather"], topk, PX, workspace=big,
+                                error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(dW, dW_big)
+    del big
+    ns = [0, 1, 31, 32, 62, 63]
+    rows = np.array([e * N + n for e in range(E) for n in ns])
+    cols = np.concatenate([np.arange(0, 32), np.arange(4096 - 16, 4096 + 16),
+                           np.arange(K - 32, K)]).astype(np.int32)
+    ref = oracle.grouped_gemm_dW(synth.bits(X), synth.bits(dY), ref_route["m_sizes"],
+                                 ref_route["gather"], topk, PX, E, rows=rows, cols=cols)
+    got = dW.reshape(E * N, K)[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).long().cuda()]
+    _assert_close(got, ref, "dW, copy area over 2 GiB")

@@ -261,9 +261,12 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     if (workspace != nullptr && (int64_t)workspace_bytes < ws_need)
         return MOEGG_EWORKSPACE;
     // Room for X's rows in expert order after the partials: gather them first.
+    // The copy is an operand of the reduction like X itself, so it must stay
+    // below 2 GiB too; a larger one keeps the gather inside the reduction.
     const int64_t xg_off = moegg::dw_gather_offset((int64_t)num_tokens * topk, num_experts, N, K);
     const int64_t xg_bytes = (int64_t)num_tokens * topk * K * 2;
     const bool use_xg = workspace != nullptr && (flags & MOEGG_PERMUTE_X) && xg_bytes > 0 &&
+                        fits((int64_t)num_tokens * topk, K) &&
                         (int64_t)workspace_bytes >= xg_off + xg_bytes;
     int cus = 0;
     if (device_cus(&cus) != 0)
@@ -314,6 +317,8 @@ size_t moegg_grouped_gemm_dW_gather_workspace_bytes(int32_t num_tokens, int32_t 
     if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
         return 0;
     const int64_t S = (int64_t)num_tokens * topk;
+    if (!fits(S, K))  // no copy: the rows are gathered inside the reduction
+        return (size_t)moegg::dw_workspace_bytes(S, num_experts, N, K);
     return (size_t)(moegg::dw_gather_offset(S, num_experts, N, K) + S * K * 2);
 }
 

@@ -88,79 +88,8 @@ __device__ __forceinline__ uint32_t dw(const uint4 &v, int d)
 // row or column is the offset kOOB (operands are limited to 2 GiB each).
 constexpr uint32_t kOOB = 0x80000000u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t as_rsrc(const u32x4_t &w)
-{
-    const uint64_t base = (uint64_t)w.x | ((uint64_t)w.y << 32);
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), (short)0, (int)w.z,
-                                             (int)w.w);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// ROWS tile rows, reduction contiguous in HBM: thread t copies chunk t % 8 of
-// rows t / 8 + i * (NT / 8).  off[i] is that chunk's byte offset at k = 0
-// (kOOB: zero row).
-template <int ROWS, int NT>
-struct DirectLoader {
-    static constexpr int PASS = NT / kChunks;
-    static constexpr int RPT = ROWS / PASS;
-    static_assert(ROWS % PASS == 0, "loader covers whole passes");
-    uint32_t off[RPT];
-    uint4 v[RPT];
-
-    __device__ __forceinline__ static int tile_row(int i) { return (threadIdx.x >> 3) + i * PASS; }
-
-    // row < 0 masks the row; row_bytes is the HBM row pitch.
-    __device__ __forceinline__ void set_row(int i, int64_t row, int64_t row_bytes)
-    {
-        off[i] = row < 0 ? kOOB : (uint32_t)(row * row_bytes) + (threadIdx.x & 7) * 16;
-    }
-
-    static constexpr bool kAsync = false;
-
-    __device__ __forceinline__ void load(const u32x4_t &w, char *, int k0, int klen)
-    {
-        const __amdgpu_buffer_rsrc_t r = as_rsrc(w);
-        const bool kin = k0 + (int)(threadIdx.x & 7) * 8 < klen;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            v[i] = buf_load16(r, kin ? off[i] : kOOB, (uint32_t)k0 * 2);
-    }
-
-    __device__ __forceinline__ void store(char *lds) const
-    {
-        const int c = threadIdx.x & 7;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            *reinterpret_cast<uint4 *>(lds + lds_swz(tile_row(i), c)) = v[i];
-        }
-    }
-};
-
-// ROWS tile rows, reduction contiguous in HBM, copied HBM -> LDS without
-// passing through registers (buffer_load_dwordx4 ... lds).  Lane l of a wave
-// writes LDS bytes [16 l, 16 l + 16) of the wave's 1 KiB window, i.e. physical
-// chunk l % 8 of window row l / 8; to land in the swizzled layout it fetches
-// the logical chunk that swizzles to it (the swizzle is an involution).  Wave
-// w, pass i fills rows 8 w + i * (NT / 8) .. + 7, so the eight lanes of a row
-// still read one whole 128-byte row segment.
-//
-// The copy is issued from inline assembly, so the compiler does not know it
-// writes LDS and does not hold back LDS reads of the other stage until it
-// lands; the mainloop waits for it explicitly (wait_vmem) before the barrier
-// that publishes the stage.  Vector-memory loads complete in issue order, so
-// any wait the compiler inserts for its own loads can only wait longer.
 // Raw buffer descriptor words (uniform): base, stride 0, num_records, format.
 __device__ __forceinline__ u32x4_t rsrc_words(const void *base, int64_t bytes)
 {
@@ -173,6 +102,14 @@ __device__ __forceinline__ u32x4_t rsrc_words(const void *base, int64_t bytes)
     return w;
 }
 
+// 16 bytes per lane copied HBM -> LDS without passing through registers
+// (buffer_load_dwordx4 ... lds): lane l writes LDS bytes [16 l, 16 l + 16)
+// from lds_addr (a wave's 1 KiB window).  The copy is issued from inline
+// assembly, so the compiler does not know it writes LDS and does not hold
+// back LDS reads of the other stage until it lands; every loop waits for it
+// explicitly (wait_vmem / wait_vmcnt) before the barrier that publishes the
+// stage.  Vector-memory loads complete in issue order, so any wait the
+// compiler inserts for its own loads can only wait longer.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16_to_lds(const u32x4_t &r, uint32_t voff, uint32_t soff,
@@ -185,12 +122,17 @@ __device__ __forceinline__ void copy16_to_lds(const u32x4_t &r, uint32_t voff, u
 }
 #pragma clang diagnostic pop
 
+// ROWS tile rows, reduction contiguous in HBM, copied with copy16_to_lds.
+// Lane l of a wave writes physical chunk l % 8 of window row l / 8; to land
+// in the swizzled layout it fetches the logical chunk that swizzles to it
+// (the swizzle is an involution).  Wave w, pass i fills rows
+// 8 w + i * (NT / 8) .. + 7, so the eight lanes of a row still read one whole
+// 128-byte row segment.
 template <int ROWS, int NT>
 struct DmaLoader {
     static constexpr int PASS = NT / kChunks;
     static constexpr int RPT = ROWS / PASS;
     static_assert(ROWS % PASS == 0, "DMA loader covers whole passes");
-    static constexpr bool kAsync = true;
     uint32_t off[RPT];
 
     __device__ __forceinline__ static int tile_row(int i) { return (threadIdx.x >> 3) + i * PASS; }
@@ -207,8 +149,6 @@ struct DmaLoader {
     {
         off[i] = row < 0 ? kOOB : (uint32_t)(row * row_bytes) + chunk() * 16;
     }
-
-    __device__ __forceinline__ void store(char *) const {}
 
     // Enqueue the copies of reduction stage k0 into the LDS stage `lds`.
     __device__ __forceinline__ void load(const u32x4_t &r, char *lds, int k0, int klen) const
@@ -244,42 +184,8 @@ __device__ __forceinline__ int tr_off(int row, int chunk)
     return row * (COLS * 2) + ((chunk ^ ((row & 3) << 2)) << 4);
 }
 
-// Copies BK reduction rows x COLS columns, 16 bytes per lane, consecutive
-// lanes along a row (whole 128-byte row segments).  rowfn(red) gives the
-// byte offset of the HBM row holding reduction index red (kOOB: zeros).
-template <int COLS, int NT>
-struct RowTileLoader {
-    static constexpr int CPR = COLS / 8;
-    static constexpr int ROWS_PER_PASS = NT / CPR;
-    static constexpr int RPT = BK / ROWS_PER_PASS;
-    static_assert(NT % CPR == 0 && BK % ROWS_PER_PASS == 0, "whole rows per pass");
-    uint4 v[RPT];
-
-    template <class RowFn>
-    __device__ __forceinline__ void load(const u32x4_t &w, int red0, int col0, int ncols,
-                                         RowFn rowfn)
-    {
-        const __amdgpu_buffer_rsrc_t r = as_rsrc(w);
-        const int col = col0 + (threadIdx.x % CPR) * 8;
-        const bool cin = col < ncols;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const uint32_t ro = rowfn(red0 + (int)threadIdx.x / CPR + i * ROWS_PER_PASS);
-            v[i] = buf_load16(r, cin ? ro + (uint32_t)col * 2 : kOOB, 0);
-        }
-    }
-
-    __device__ __forceinline__ void store(char *lds) const
-    {
-        const int c = threadIdx.x % CPR;
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            *reinterpret_cast<uint4 *>(lds + tr_off<COLS>((int)threadIdx.x / CPR + i * ROWS_PER_PASS,
-                                                           c)) = v[i];
-    }
-};
-
-// The same row-major tile, copied HBM -> LDS without registers.  A wave's
+// A row-major tile (BK reduction rows of COLS columns) copied HBM -> LDS
+// without registers.  A wave's
 // 1 KiB window is RW = 64 / (COLS / 8) whole rows; lane l writes physical
 // chunk l % (COLS / 8) of window row l / (COLS / 8) and therefore fetches the
 // logical chunk that the row swizzle maps there.
@@ -320,8 +226,6 @@ struct TileDmaLoader {
         for (int i = 0; i < RPT; ++i)
             raw[i] = rawfn(red_base + row_of(i));
     }
-
-    __device__ __forceinline__ void store(char *) const {}
 
     // Turn the raw indices fetched last into byte offsets: fin(red, raw) ->
     // HBM row (-1: zeros); row_bytes is the HBM pitch.  Call before issuing
@@ -493,50 +397,25 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[C::FM][C::FN])
                 acc[i][j][r] = 0.0f;
 }
 
-// Every operand is copied HBM -> LDS without passing through registers
-// (DmaLoader, TileDmaLoader).  Setting one of these switches to 0 builds the
-// register-staged loader (DirectLoader, RowTileLoader) instead, for
-// comparison; on MI355X the copies measured faster wherever they are used.
-#ifndef MOEGG_FWD_DMA
-#define MOEGG_FWD_DMA 1
-#endif
-#ifndef MOEGG_DX_DMA
-#define MOEGG_DX_DMA 1
-#endif
-#ifndef MOEGG_TILE_DMA
-#define MOEGG_TILE_DMA 1
-#endif
-#ifndef MOEGG_GROUPS_DMA
-#define MOEGG_GROUPS_DMA 1
-#endif
-template <int ROWS, int NT, bool ASYNC>
-using RowLoader =
-    typename std::conditional<ASYNC, DmaLoader<ROWS, NT>, DirectLoader<ROWS, NT>>::type;
-
-// Two LDS stages.  Per stage s: start the HBM reads of stage s+1 (copies
-// straight into the other LDS stage, or loads into registers), run the MFMAs
-// of stage s from LDS, write register-staged data of stage s+1 to LDS, wait
-// for this wave's reads and copies, and barrier.  load(s, As, Bs) starts the
-// reads of stage s; store(As, Bs) writes register-staged data.  The other
-// stage was last read before the previous barrier, so it is free to fill.
-template <class C, bool PIPE, bool A_TR, bool B_TR, bool PART, class Load, class Store>
+// Two LDS stages.  Per stage s: start the copies of stage s+1 straight into
+// the other LDS stage, run the MFMAs of stage s from LDS, wait for this
+// wave's copies, and barrier.  load(s, As, Bs) starts the copies of stage s.
+// The other stage was last read before the previous barrier, so it is free
+// to fill.
+template <class C, bool PIPE, bool A_TR, bool B_TR, bool PART, class Load>
 __device__ __forceinline__ void mainloop_body(char *st0, char *st1, int nsteps,
-                                              f32x16_t (&acc)[C::FM][C::FN], Load &load,
-                                              Store &store, int wm, int wn, int ib)
+                                              f32x16_t (&acc)[C::FM][C::FN], Load &load, int wm,
+                                              int wn, int ib)
 {
     load(0, st0, st0 + C::A_BYTES);
-    store(st0, st0 + C::A_BYTES);
     wait_vmem();
     __syncthreads();
     for (int s = 0; s < nsteps; ++s) {
         char *cur = (s & 1) ? st1 : st0;
         char *nxt = (s & 1) ? st0 : st1;
-        const bool more = s + 1 < nsteps;
-        if (more)
+        if (s + 1 < nsteps)
             load(s + 1, nxt, nxt + C::A_BYTES);
         mma_stage<C, PIPE, A_TR, B_TR, PART>(cur, cur + C::A_BYTES, acc, wm, wn, ib);
-        if (more)
-            store(nxt, nxt + C::A_BYTES);
         wait_vmem();
         __syncthreads();
     }
@@ -545,9 +424,9 @@ __device__ __forceinline__ void mainloop_body(char *st0, char *st1, int nsteps,
 // rows: tile rows (A side) holding real data.  A wave whose 32-row blocks
 // are all real runs the branch-free body; a wave of a ragged tail tile skips
 // the MFMAs and A reads of its padding blocks (the barriers are the same).
-template <class C, bool PIPE, bool A_TR, bool B_TR, class Load, class Store>
+template <class C, bool PIPE, bool A_TR, bool B_TR, class Load>
 __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
-                                         f32x16_t (&acc)[C::FM][C::FN], Load load, Store store,
+                                         f32x16_t (&acc)[C::FM][C::FN], Load load,
                                          int rows = C::BM)
 {
     const int wave = threadIdx.x / kWave;
@@ -557,9 +436,9 @@ __device__ __forceinline__ void mainloop(char *st0, char *st1, int nsteps,
     const int ib = __builtin_amdgcn_readfirstlane(
         min(C::FM, max(0, (rows - wm * C::TM + 31) / 32)));
     if (ib == C::FM)
-        mainloop_body<C, PIPE, A_TR, B_TR, false>(st0, st1, nsteps, acc, load, store, wm, wn, ib);
+        mainloop_body<C, PIPE, A_TR, B_TR, false>(st0, st1, nsteps, acc, load, wm, wn, ib);
     else
-        mainloop_body<C, PIPE, A_TR, B_TR, true>(st0, st1, nsteps, acc, load, store, wm, wn, ib);
+        mainloop_body<C, PIPE, A_TR, B_TR, true>(st0, st1, nsteps, acc, load, wm, wn, ib);
 }
 
 // ---------------------------------------------------------------------------
@@ -1497,8 +1376,8 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             rsrc_words(a.W + (int64_t)e * a.N * row_bytes, (int64_t)a.N * row_bytes);
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        RowLoader<C::BM, C::NT, MOEGG_FWD_DMA != 0> la;
-        RowLoader<C::BN, C::NT, MOEGG_FWD_DMA != 0> lb;
+        DmaLoader<C::BM, C::NT> la;
+        DmaLoader<C::BN, C::NT> lb;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], row_bytes);
@@ -1515,10 +1394,6 @@ __global__ __launch_bounds__(C::NT) void fwd_kernel(FwdParams a)
             [&](int s, char *As, char *Bs) {
                 la.load(xr, As, s * BK, a.K);
                 lb.load(wr, Bs, s * BK, a.K);
-            },
-            [&](char *As, char *Bs) {
-                la.store(As);
-                lb.store(Bs);
             },
             rows);
         if constexpr (GATED)
@@ -1642,7 +1517,7 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
             }
             continue;
         }
-        RowLoader<C::BM, C::NT, MOEGG_DX_DMA != 0> la;
+        DmaLoader<C::BM, C::NT> la;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i)
             la.set_row(i, s_src[la.tile_row(i)], dy_row);
@@ -1650,40 +1525,20 @@ __global__ __launch_bounds__(C::NT) void dx_kernel(DxParams a)
         const int u0 = tail ? part * nsteps / tp.P : 0;
         const int u1 = tail ? (part + 1) * nsteps / tp.P : nsteps;
         zero_acc<C>(acc);
-        if constexpr (MOEGG_TILE_DMA != 0) {
-            TileDmaLoader<C::BN, C::NT> lb;
-            auto wraw = [](int n) -> int { return n; };
-            auto wfin = [=](int n, int) -> int { return n < N ? n : -1; };
-            lb.fetch(u0 * BK, wraw);
-            mainloop<C, true, false, true>(
-                st0, st1, u1 - u0, acc,
-                [&](int s, char *As, char *Bs) {
-                    lb.prepare(k0, a.K, w_row, wfin);
-                    __builtin_amdgcn_sched_barrier(0);
-                    la.load(dyr, As, (s + u0) * BK, a.N);
-                    lb.issue(wr, Bs);
-                    lb.fetch((s + u0 + 1) * BK, wraw);
-                },
-                [&](char *As, char *Bs) {
-                    la.store(As);
-                    lb.store(Bs);
-                },
+        TileDmaLoader<C::BN, C::NT> lb;
+        auto wraw = [](int n) -> int { return n; };
+        auto wfin = [=](int n, int) -> int { return n < N ? n : -1; };
+        lb.fetch(u0 * BK, wraw);
+        mainloop<C, true, false, true>(
+            st0, st1, u1 - u0, acc,
+            [&](int s, char *As, char *Bs) {
+                lb.prepare(k0, a.K, w_row, wfin);
+                __builtin_amdgcn_sched_barrier(0);
+                la.load(dyr, As, (s + u0) * BK, a.N);
+                lb.issue(wr, Bs);
+                lb.fetch((s + u0 + 1) * BK, wraw);
+            },
             rows);
-        } else {
-            RowTileLoader<C::BN, C::NT> lb;
-            auto wrowfn = [=](int n) -> uint32_t { return n < N ? (uint32_t)(n * w_row) : kOOB; };
-            mainloop<C, true, false, true>(
-                st0, st1, u1 - u0, acc,
-                [&](int s, char *As, char *) {
-                    la.load(dyr, As, (s + u0) * BK, a.N);
-                    lb.load(wr, (s + u0) * BK, k0, a.K, wrowfn);
-                },
-                [&](char *As, char *Bs) {
-                    la.store(As);
-                    lb.store(Bs);
-                },
-            rows);
-        }
         if (tail) {
             epilogue_f32<C>(acc, s_dst, partial, C::BN, 0, C::BN);
             __syncthreads();
@@ -1709,9 +1564,6 @@ constexpr int kGroupK = 8;
 // each wait can count them.  Measured: fine-grained dW 0.404 -> 0.368 ms,
 // decode-shaped dW 0.113 -> 0.105 ms; the Mixtral shape is unchanged (its
 // copies are bound by their rate, not by how far ahead they are issued).
-#ifndef MOEGG_DW_SLOTS
-#define MOEGG_DW_SLOTS 1
-#endif
 constexpr int kDwSlot = 32;      // reduction rows per slot
 constexpr int kDwSlots = 4;
 constexpr int kDwGather = 1024;  // gather entries staged per segment
@@ -1843,7 +1695,7 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
         const int nsteps = (mc + BK - 1) / BK;
-        if constexpr (MOEGG_TILE_DMA != 0 && MOEGG_DW_SLOTS != 0) {
+        {
             static_assert(kDwSlots * 2 * C::BM * kDwSlot * 2 <= 2 * C::STAGE &&
                               C::BM == C::BN && kMaxExperts + 1 >= kDwGather,
                           "four slots in the two stages; gather entries in s_tstart");
@@ -1922,94 +1774,6 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
             }
             if (bad)
                 raise_error(err, kErrGather);
-        } else if constexpr (MOEGG_TILE_DMA != 0) {
-            // Row index of reduction index red in dY and in X (-1: zeros),
-            // without branches.  raw: the gather entry (read clamped into the
-            // expert's rows) or the sorted position; fin: validity and, for
-            // X under permute_x, the token row g / topk.  A gather entry
-            // outside [0, S) gives zeros and is reported once per tile.
-            const FastDiv tdiv = a.topk_div;
-            const uint32_t Su = (uint32_t)S;
-            bool bad = false;
-            auto graw = [=](int red) -> int {
-                const int64_t p = start + min(red, mc - 1);
-                if constexpr (PX || PY)
-                    return gather[p];
-                return (int)p;
-            };
-            auto pos = [=](int red) -> int { return start + red; };
-            auto dyfin = [&](int red, int g) -> int {
-                const bool ok = !PY || (uint32_t)g < Su;
-                bad |= red < mc && !ok;
-                return (red < mc && ok) ? (PY ? g : start + red) : -1;
-            };
-            auto xfin = [&](int red, int g) -> int {
-                const bool ok = !PX || (uint32_t)g < Su;
-                bad |= red < mc && !ok;
-                return (red < mc && ok) ? (PX ? fast_div((uint32_t)g, tdiv) : start + red) : -1;
-            };
-            TileDmaLoader<C::BM, C::NT> la;
-            TileDmaLoader<C::BN, C::NT> lb;
-            if (nsteps > 0) {
-                if constexpr (PY)
-                    la.fetch(0, graw);
-                else
-                    la.fetch(0, pos);
-                if constexpr (PX)
-                    lb.fetch(0, graw);
-                else
-                    lb.fetch(0, pos);
-                mainloop<C, true, true, true>(
-                    st0, st1, nsteps, acc,
-                    [&](int s, char *As, char *Bs) {
-                        la.prepare(n0, a.N, dy_row, dyfin);
-                        lb.prepare(k0, a.K, x_row, xfin);
-                        __builtin_amdgcn_sched_barrier(0);
-                        la.issue(dyr, As);
-                        lb.issue(xr, Bs);
-                        if constexpr (PY)
-                            la.fetch((s + 1) * BK, graw);
-                        else
-                            la.fetch((s + 1) * BK, pos);
-                        if constexpr (PX)
-                            lb.fetch((s + 1) * BK, graw);
-                        else
-                            lb.fetch((s + 1) * BK, pos);
-                    },
-                    [&](char *, char *) {},
-                    min(C::BM, a.N - n0));
-            }
-            if (bad)
-                raise_error(err, kErrGather);
-        } else {
-            const bool px = PX, py = PY;
-            auto dyrowfn = [=](int red) -> uint32_t {
-                if (red >= mc)
-                    return kOOB;
-                const int64_t p = start + red;
-                const int q = py ? checked_gather(gather, p, S, err) : (int)p;
-                return q >= 0 ? (uint32_t)(q * dy_row) : kOOB;
-            };
-            auto xrowfn = [=](int red) -> uint32_t {
-                if (red >= mc)
-                    return kOOB;
-                const int64_t p = start + red;
-                const int g = px ? checked_gather(gather, p, S, err) : (int)p;
-                return g >= 0 ? (uint32_t)((px ? g / topk : g) * x_row) : kOOB;
-            };
-            RowTileLoader<C::BM, C::NT> la;
-            RowTileLoader<C::BN, C::NT> lb;
-            mainloop<C, true, true, true>(
-                st0, st1, nsteps, acc,
-                [&](int s, char *, char *) {
-                    la.load(dyr, s * BK, n0, a.N, dyrowfn);
-                    lb.load(xr, s * BK, k0, a.K, xrowfn);
-                },
-                [&](char *As, char *Bs) {
-                    la.store(As);
-                    lb.store(Bs);
-                },
-            min(C::BM, a.N - n0));
         }
         if (split) {
             const int poff = __builtin_amdgcn_readfirstlane(s_poff[pos]);
@@ -2106,7 +1870,7 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
         const int64_t x_row = (int64_t)g.ldx * 2, w_row = (int64_t)g.ldw * 2;
         const u32x4_t xr = rsrc_words(g.x, (int64_t)g.m * x_row);
         const u32x4_t wr = rsrc_words(g.w, (int64_t)(TRANS_B ? g.n : g.k) * w_row);
-        RowLoader<C::BM, C::NT, MOEGG_GROUPS_DMA != 0> la;
+        DmaLoader<C::BM, C::NT> la;
 #pragma unroll
         for (int i = 0; i < la.RPT; ++i) {
             const int r = la.tile_row(i);
@@ -2117,7 +1881,7 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
         const int nsteps = (g.k + BK - 1) / BK;
         const int kk = g.k;
         if constexpr (TRANS_B) {
-            RowLoader<C::BN, C::NT, MOEGG_GROUPS_DMA != 0> lb;
+            DmaLoader<C::BN, C::NT> lb;
 #pragma unroll
             for (int i = 0; i < lb.RPT; ++i) {
                 const int r = lb.tile_row(i);
@@ -2129,28 +1893,22 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
                     la.load(xr, As, s * BK, kk);
                     lb.load(wr, Bs, s * BK, kk);
                 },
-                [&](char *As, char *Bs) {
-                    la.store(As);
-                    lb.store(Bs);
-                },
-            min(C::BM, g.m - m0));
+                min(C::BM, g.m - m0));
         } else {
-            RowTileLoader<C::BN, C::NT> lb;
-            auto wrowfn = [=](int red) -> uint32_t {
-                return red < kk ? (uint32_t)(red * w_row) : kOOB;
-            };
+            TileDmaLoader<C::BN, C::NT> lb;
             const int n = g.n;
             mainloop<C, true, false, true>(
                 st0, st1, nsteps, acc,
-                [&](int s, char *As, char *) {
+                [&](int s, char *As, char *Bs) {
+                    lb.prepare_rows(n0, n, w_row, [&](int row) {
+                        const int red = s * BK + row;
+                        return red < kk ? red : -1;
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
                     la.load(xr, As, s * BK, kk);
-                    lb.load(wr, s * BK, n0, n, wrowfn);
+                    lb.issue(wr, Bs);
                 },
-                [&](char *As, char *Bs) {
-                la.store(As);
-                lb.store(Bs);
-            },
-            min(C::BM, g.m - m0));
+                min(C::BM, g.m - m0));
         }
         epilogue_bf16<C>(st0, st1, acc, s_dst, nullptr, static_cast<char *>(g.y), g.ldy, n0, g.n);
     }
@@ -2364,12 +2122,28 @@ int64_t dw_gather_offset(int64_t S, int E, int N, int K)
 // for the row gather inside dW, with the same result bit for bit: the
 // scattered row reads cost dW's copy path more than one streaming pass
 // costs.  One workgroup per row at a time; an entry outside [0, S) gives a
-// zero row and is reported, as the gather inside dW does.  Plain stores:
-// dW reads the copy right after.
+// zero row and is reported, as the gather inside dW does.  Only the
+// positions the reduction reads are copied: those below the sum of m_sizes
+// (negative sizes as 0, clipped to S, as the reduction's tables take them),
+// so the entries routing leaves at -1 for dropped slots are not touched.
+// Plain stores: dW reads the copy right after.
 __global__ __launch_bounds__(256) void gather_x_kernel(DwParams a)
 {
+    __shared__ long long s_part[256 / kWave];
+    long long part = 0;
+    for (int e = threadIdx.x; e < a.E; e += blockDim.x)
+        part += max(a.m_sizes[e], 0);
+    for (int d = kWave / 2; d > 0; d >>= 1)
+        part += __shfl_xor(part, d, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        s_part[threadIdx.x / kWave] = part;
+    __syncthreads();
+    int64_t rows = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w)
+        rows += s_part[w];
+    rows = min(rows, a.S);
     const int cpr = a.K / 8;  // 16-byte chunks per row
-    for (int64_t p = blockIdx.x; p < a.S; p += gridDim.x) {
+    for (int64_t p = blockIdx.x; p < rows; p += gridDim.x) {
         const int g = __builtin_amdgcn_readfirstlane(a.gather[p]);
         const bool ok = g >= 0 && g < a.S;
         if (!ok && threadIdx.x == 0)

@@ -117,6 +117,32 @@ moegg_status moegg_route(const int32_t *topk_ids, int32_t num_tokens, int32_t to
                          int32_t *gather_idx, int32_t *scatter_idx, void *workspace,
                          size_t workspace_bytes, int32_t *error_flags, void *stream);
 
+/* Size of the device array moegg_route_noalloc keeps its counts in. */
+#define MOEGG_ROUTE_NOALLOC_MAX_BYTES (1u << 20)
+
+/*
+ * moegg_route_noalloc -- moegg_route without a workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no allocating routine.
+ *
+ * The per-chunk counts go to a static device array of
+ * MOEGG_ROUTE_NOALLOC_MAX_BYTES bytes that the library holds on every device
+ * it runs on until the process ends (its address is looked up on the first
+ * call on each device).  A call with moegg_route_workspace_bytes(T * topk, E)
+ * larger than that (e.g. more than 65,536 slots with E = 1024, or more than
+ * 2^21 slots with E = 32) returns MOEGG_EWORKSPACE before anything is
+ * enqueued.  All calls on one device share the array: calls that may run at
+ * the same time on that GPU (streams without ordering between them) race and
+ * give wrong results; calls ordered on one stream do not, since each call
+ * writes every count it reads.  Otherwise the same arguments, results and
+ * errors as moegg_route.
+ */
+moegg_status moegg_route_noalloc(const int32_t *topk_ids, int32_t num_tokens, int32_t topk,
+                                 int32_t num_experts, int32_t block_m, int32_t *m_sizes,
+                                 int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets,
+                                 int32_t *gather_idx, int32_t *scatter_idx, int32_t *error_flags,
+                                 void *stream);
+
 /*
  * moegg_grouped_gemm_fwd -- Y_e = X_e W_e^T for every expert, one launch.
  *

@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moegg_route_workspace_bytes.restype = sz
     lib.moegg_route.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.moegg_route.restype = ctypes.c_int
+    lib.moegg_route_noalloc.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moegg_route_noalloc.restype = ctypes.c_int
     lib.moegg_grouped_gemm_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, vp,
                                            vp, vp]
     lib.moegg_grouped_gemm_fwd.restype = ctypes.c_int
@@ -156,6 +158,28 @@ def moe_route(topk_ids: torch.Tensor, num_experts: int, block_m: int = 128, *, o
         _ptr(out.get("padded_offsets")), _ptr(out.get("tile_offsets")), _ptr(out["gather"]),
         _ptr(out.get("scatter")), _ptr(workspace), workspace.numel(), _ptr(error_flags),
         _stream(stream)), "moegg_route")
+    return out
+
+
+ROUTE_NOALLOC_MAX_BYTES = 1 << 20
+
+
+def moe_route_noalloc(topk_ids: torch.Tensor, num_experts: int, block_m: int = 128, *, out,
+                      error_flags=None, stream=None):
+    """moe_route without a workspace (moegg_route_noalloc): the library keeps
+    the per-chunk counts in its own static device array, so the call
+    allocates nothing.  `out` holds the output tensors, as moe_route returns
+    them (m_sizes and offsets required; padded_offsets, tile_offsets and
+    scatter optional); calls that overlap on one GPU race."""
+    lib = load_library()
+    ids = _device_tensor(topk_ids, torch.int32, "topk_ids")
+    topk = ids.shape[-1] if ids.dim() == 2 else 1
+    T = ids.numel() // topk
+    _check(lib.moegg_route_noalloc(
+        _ptr(ids), T, topk, int(num_experts), int(block_m), _ptr(out["m_sizes"]),
+        _ptr(out["offsets"]), _ptr(out.get("padded_offsets")), _ptr(out.get("tile_offsets")),
+        _ptr(out["gather"]), _ptr(out.get("scatter")), _ptr(error_flags), _stream(stream)),
+        "moegg_route_noalloc")
     return out
 
 

@@ -129,6 +129,33 @@ moegg_status moegg_route(const int32_t *topk_ids, int32_t num_tokens, int32_t to
                                         static_cast<hipStream_t>(stream)));
 }
 
+moegg_status moegg_route_noalloc(const int32_t *topk_ids, int32_t num_tokens, int32_t topk,
+                                 int32_t num_experts, int32_t block_m, int32_t *m_sizes,
+                                 int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets,
+                                 int32_t *gather_idx, int32_t *scatter_idx, int32_t *error_flags,
+                                 void *stream)
+{
+    if (num_tokens < 0 || topk < 1 || num_experts < 1 || num_experts > MOEGG_MAX_EXPERTS ||
+        block_m < 1)
+        return MOEGG_ESHAPE;
+    const int64_t S = (int64_t)num_tokens * topk;
+    if (S > INT32_MAX)
+        return MOEGG_ESHAPE;
+    if (m_sizes == nullptr || offsets == nullptr)
+        return MOEGG_EINVAL;
+    if (S > 0 && (topk_ids == nullptr || gather_idx == nullptr))
+        return MOEGG_EINVAL;
+    if (moegg_route_workspace_bytes(S, num_experts) > MOEGG_ROUTE_NOALLOC_MAX_BYTES)
+        return MOEGG_EWORKSPACE;  // more per-chunk counts than the static array holds
+    int32_t *counts = nullptr;
+    hipError_t e = moegg::route_scratch(&counts);
+    if (e != hipSuccess)
+        return MOEGG_EHIP;
+    return from_hip(moegg::route_launch(topk_ids, S, num_experts, block_m, m_sizes, offsets,
+                                        padded_offsets, tile_offsets, gather_idx, scatter_idx,
+                                        counts, error_flags, static_cast<hipStream_t>(stream)));
+}
+
 moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t *m_sizes,
                                     const int32_t *gather_idx, const float *topk_weights,
                                     int32_t num_tokens, int32_t topk, int32_t num_experts,

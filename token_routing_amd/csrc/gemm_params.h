@@ -153,6 +153,7 @@ hipError_t combine_launch(const CombineParams &p, hipStream_t stream);
 hipError_t combine_bwd_launch(const CombineBwdParams &p, hipStream_t stream);
 
 int64_t route_chunks(int64_t S);
+hipError_t route_scratch(int32_t **out);
 hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32_t *m_sizes,
                         int32_t *offsets, int32_t *padded_offsets, int32_t *tile_offsets,
                         int32_t *gather, int32_t *scatter, int32_t *counts, int32_t *err,

@@ -23,6 +23,8 @@
 //      a slot's position is its cursor plus the number of lower lanes with
 //      the same expert.  Chunks are in slot order and lanes are in slot
 //      order, so the result is the stable counting sort, bit for bit.
+#include <mutex>
+
 #include "common.h"
 
 #include "gemm_params.h"
@@ -323,6 +325,41 @@ static int bits_for(int E)
 int64_t route_chunks(int64_t S)
 {
     return (S + kSlotsPerWave - 1) / kSlotsPerWave;
+}
+
+// Per-chunk counts of moegg_route_noalloc: a device array the library holds
+// on every device it runs on (one copy per device, at its own address) until
+// the process ends.  route_count writes every count route_scan and
+// route_scatter read, so the array needs no clearing between calls.
+static __device__ __align__(256) int32_t scratch[MOEGG_ROUTE_NOALLOC_MAX_BYTES / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch[kMaxScratchDevices];  // device address of `scratch`, per device
+}  // namespace
+
+// Device address of the current device's `scratch`, looked up once per
+// device (host code must not pass the array's own name to a kernel: that is
+// a host-side stand-in, not a device address).
+hipError_t route_scratch(int32_t **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch[dev] = static_cast<int32_t *>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
 }
 
 hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32_t *m_sizes,

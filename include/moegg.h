@@ -264,7 +264,8 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
  * reductions, for these sizes: a small header plus fp32 [N, K] partials for
  * fewer than 2 S / split_rows chunks, where split_rows is about
  * S * ceil(N/256) * ceil(K/256) / 768 rows (at least 256).  0 when no
- * expert can hold more than split_rows rows (then the workspace is unused).
+ * expert can hold more than split_rows rows, or when S <= 1024 (reductions
+ * that short are never split); the workspace is then unused.
  */
 size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
                                              int32_t num_experts, int32_t N, int32_t K);

@@ -109,6 +109,9 @@ def test_dw_workspace(lib):
     # Mixtral-shaped layer: an expert can never exceed the chunk length
     assert lib.moegg_grouped_gemm_dW_workspace_bytes(4096, 2, 8, 28672, 4096) == 0
     assert lib.moegg_grouped_gemm_dW_workspace_bytes(-1, 2, 8, 64, 64) == 0
+    # a decode step (64 tokens, top-8: 512 slots) is never split
+    assert lib.moegg_grouped_gemm_dW_workspace_bytes(64, 8, 128, 2048, 768) == 0
+    assert lib.moegg_grouped_gemm_dW_workspace_bytes(129, 8, 128, 2048, 768) > 0
     # a workspace smaller than needed is rejected before anything runs
     assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 8192, 8, 128, 2048, 768, PY, FAKE,
                                      FAKE, 1024, None, None) == EWS

@@ -122,6 +122,15 @@ __device__ __forceinline__ void copy16_to_lds(const u32x4_t &r, uint32_t voff, u
 }
 #pragma clang diagnostic pop
 
+// LDS byte address of a pointer into a __shared__ array: the low 32 bits of
+// its flat address (the shared aperture is the high half).  Taken by
+// truncation rather than an address-space cast, whose null check the
+// compiler can mislower when the address is a constant under a branch.
+__device__ __forceinline__ uint32_t lds_u32(const void *p)
+{
+    return (uint32_t)reinterpret_cast<uintptr_t>(p);
+}
+
 // ROWS tile rows, reduction contiguous in HBM, copied with copy16_to_lds.
 // Lane l of a wave writes physical chunk l % 8 of window row l / 8; to land
 // in the swizzled layout it fetches the logical chunk that swizzles to it
@@ -155,8 +164,7 @@ struct DmaLoader {
     {
         const bool kin = k0 + chunk() * 8 < klen;
         const uint32_t wave_row = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * 8;
-        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(
-            (__attribute__((address_space(3))) char *)lds);
+        const uint32_t base = lds_u32(lds);
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
             copy16_to_lds(r, kin ? off[i] : kOOB, (uint32_t)k0 * 2,
@@ -266,8 +274,7 @@ struct TileDmaLoader {
     // Copy the prepared rows into the LDS tile.
     __device__ __forceinline__ void issue(const u32x4_t &r, char *lds) const
     {
-        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(
-            (__attribute__((address_space(3))) char *)lds);
+        const uint32_t base = lds_u32(lds);
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
             copy16_to_lds(r, voff[i], 0,
@@ -491,9 +498,7 @@ struct SlotCopier {
     {
         const int lc = (lane() & 3) ^ ((lane() >> 4) & 3);
         kc = lc * 8;
-        lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(
-                   (__attribute__((address_space(3))) char *)slot0_part)) +
-               first_row * (SK * 2);
+        lds0 = __builtin_amdgcn_readfirstlane(lds_u32(slot0_part)) + first_row * (SK * 2);
     }
     __device__ __forceinline__ void set_row(int j, int64_t hbm_row, int64_t row_bytes)
     {
@@ -762,6 +767,58 @@ __device__ __forceinline__ void quad_body(const char *smem, int nslots, f32x16_t
     quad_slot<C, PART, false, false, 0>(smem, q, acc, f, copy, ib, fa, fb);
 }
 
+// NST LDS stages of BK (a ring): the copies of stage s + NST - 1 are issued
+// at stage s, right after the barrier that ends every wave's reads of stage
+// s - 1, whose buffer they fill; so each stage's copies have NST - 1 stages of
+// MFMAs to land instead of one.  load(s, As, Bs) issues this wave's CPS copies
+// of stage s (the only vector-memory operations of the loop: the waits count
+// them).  Leaves LDS free for the epilogue.
+template <class C, int NST, bool A_TR, bool B_TR, int CPS, bool PART, class Load>
+__device__ __forceinline__ void ring_body(char *smem, int nsteps, f32x16_t (&acc)[C::FM][C::FN],
+                                          Load &load, int wm, int wn, int ib)
+{
+    static_assert(NST >= 2 && NST <= 4 && (NST & (NST - 1)) == 0, "2 or 4 stages");
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int q = 0; q < NST - 1 && q < nsteps; ++q)
+        load(q, smem + q * C::STAGE, smem + q * C::STAGE + C::A_BYTES);
+    for (int s = 0; s < nsteps; ++s) {
+        const int pending = min(NST - 2, nsteps - 1 - s);  // stages issued after s
+        if (pending >= 2)
+            wait_vmcnt<2 * CPS>();
+        else if (pending == 1)
+            wait_vmcnt<CPS>();
+        else
+            wait_vmcnt<0>();
+        wait_lds();
+        wg_barrier();
+        if (s + NST - 1 < nsteps) {
+            char *b = smem + ((s + NST - 1) & (NST - 1)) * C::STAGE;
+            load(s + NST - 1, b, b + C::A_BYTES);
+        }
+        const char *cur = smem + (s & (NST - 1)) * C::STAGE;
+        mma_stage<C, true, A_TR, B_TR, PART>(cur, cur + C::A_BYTES, acc, wm, wn, ib);
+    }
+    wait_lds();
+    __syncthreads();
+}
+
+template <class C, int NST, bool A_TR, bool B_TR, int CPS, class Load>
+__device__ __forceinline__ void mainloop_ring(char *smem, int nsteps,
+                                              f32x16_t (&acc)[C::FM][C::FN], Load load,
+                                              int rows = C::BM)
+{
+    const int wave = threadIdx.x / kWave;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    if (nsteps <= 0)
+        return;
+    const int ib = __builtin_amdgcn_readfirstlane(
+        min(C::FM, max(0, (rows - wm * C::TM + 31) / 32)));
+    if (ib == C::FM)
+        ring_body<C, NST, A_TR, B_TR, CPS, false>(smem, nsteps, acc, load, wm, wn, ib);
+    else
+        ring_body<C, NST, A_TR, B_TR, CPS, true>(smem, nsteps, acc, load, wm, wn, ib);
+}
+
 // A copy callback f(q, buf, n) without row-index prefetching.
 template <class F>
 struct PlainCopy {
@@ -821,9 +878,7 @@ struct SlotTileCopier {
         const int lane = threadIdx.x & (kWave - 1);
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
         row_bytes = row_bytes_;
-        lds0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(
-                   (__attribute__((address_space(3))) char *)slot0_part)) +
-               wave * NC * kWave * 16;
+        lds0 = __builtin_amdgcn_readfirstlane(lds_u32(slot0_part)) + wave * NC * kWave * 16;
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
             const int r = (wave * NC + j) * RW + lane / CPR;
@@ -1683,6 +1738,23 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         const int start = __builtin_amdgcn_readfirstlane(s_roff[e]) + chunk * cr;
         const int mc = max(0, min(cr, m_e - chunk * cr));
 
+        if (m_e == 0) {
+            // An expert without rows: its tile of dW is zeros, stored as 16-byte
+            // row segments straight from registers (no copies, MFMAs or LDS
+            // staging; every thread of the workgroup takes this branch).
+            const int esz = f32out ? 4 : 2;
+            const int cpr = min(C::BN, a.K - k0) * esz / 16;  // K is a multiple of 8
+            const int nrows = min(C::BM, a.N - n0);
+            char *const base = a.dW + (((int64_t)e * a.N + n0) * a.K + k0) * esz;
+            const u32x4_nt_t z = {0u, 0u, 0u, 0u};
+            for (int idx = threadIdx.x; idx < nrows * cpr; idx += C::NT) {
+                const int r = idx / cpr, c = idx % cpr;
+                __builtin_nontemporal_store(
+                    z, reinterpret_cast<u32x4_nt_t *>(base + (int64_t)r * a.K * esz + c * 16));
+            }
+            continue;
+        }
+
         __syncthreads();
         for (int i = threadIdx.x; i < C::BM; i += C::NT)
             s_dst[i] = (n0 + i < a.N) ? (split ? 0 : e * a.N) + n0 + i : -1;
@@ -1691,10 +1763,8 @@ __global__ __launch_bounds__(C::NT) void dw_kernel(DwParams a)
         const int64_t S = a.S;
         const int32_t *gather = a.gather;
         int32_t *err = a.err;
-        const int topk = a.topk;
         f32x16_t acc[C::FM][C::FN];
         zero_acc<C>(acc);
-        const int nsteps = (mc + BK - 1) / BK;
         {
             static_assert(kDwSlots * 2 * C::BM * kDwSlot * 2 <= 2 * C::STAGE &&
                               C::BM == C::BN && kMaxExperts + 1 >= kDwGather,
@@ -1835,11 +1905,17 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(DwParams a)
 // Explicit groups: y_g = x_g @ w_g
 // ---------------------------------------------------------------------------
 
+// The groups are few short products (the dual-expert layer: one tile per CU,
+// 16 stages over K = 1024): a tile's copies of one stage cannot hide their
+// own latency behind one stage of MFMAs, so the groups run a four-stage ring.
+constexpr int kGroupStages = 4;
+
 template <class C, bool TRANS_B>
 __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
 {
-    __shared__ __attribute__((aligned(16))) char st0[C::STAGE];
-    __shared__ __attribute__((aligned(16))) char st1[C::STAGE];
+    constexpr int NST = kGroupStages;
+    __shared__ __attribute__((aligned(16))) char smem[NST * C::STAGE];
+    char *const st0 = smem, *const st1 = smem + C::STAGE;
     __shared__ int s_tstart[MOEGG_MAX_GROUPS + 1];
     __shared__ int s_dst[C::BM];
 
@@ -1887,8 +1963,8 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
                 const int r = lb.tile_row(i);
                 lb.set_row(i, n0 + r < g.n ? n0 + r : -1, w_row);
             }
-            mainloop<C, true, false, false>(
-                st0, st1, nsteps, acc,
+            mainloop_ring<C, NST, false, false, decltype(la)::RPT + decltype(lb)::RPT>(
+                smem, nsteps, acc,
                 [&](int s, char *As, char *Bs) {
                     la.load(xr, As, s * BK, kk);
                     lb.load(wr, Bs, s * BK, kk);
@@ -1897,8 +1973,8 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
         } else {
             TileDmaLoader<C::BN, C::NT> lb;
             const int n = g.n;
-            mainloop<C, true, false, true>(
-                st0, st1, nsteps, acc,
+            mainloop_ring<C, NST, false, true, decltype(la)::RPT + decltype(lb)::RPT>(
+                smem, nsteps, acc,
                 [&](int s, char *As, char *Bs) {
                     lb.prepare_rows(n0, n, w_row, [&](int row) {
                         const int red = s * BK + row;
@@ -1938,7 +2014,10 @@ using DwCfg = Cfg<MOEGG_DW_CFG>;
 using SmallCfg = Cfg<MOEGG_SMALL_CFG>;   // few rows per expert: stream the weights
 using DxSmallCfg = Cfg<32, 128, 1, 4>;     // the same for dX
 using SmallGatedCfg = Cfg<32, 256, 1, 4>;  // the same with two blocks per wave to pair
-using GroupCfg = Cfg<128, 128, 2, 2>;    // small explicit groups: more tiles
+// Small explicit groups: tiles of 64 x 128 so that the dual-expert layer's
+// 256 tiles cover every CU (128 x 128 tiles: 15.4 us against 11.9 us there;
+// each tile's copies, about 0.4 MB over K = 1024, bound a CU's time).
+using GroupCfg = Cfg<64, 128, 1, 4>;
 
 // Explicit instantiations: every kernel the launchers use is emitted here.
 template __global__ void fwd_kernel<BigCfg, false>(FwdParams);
@@ -2087,10 +2166,16 @@ hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 #define MOEGG_DW_SPLIT_ITEMS 3
 #endif
 constexpr int kSplitCus = 256, kSplitItems = MOEGG_DW_SPLIT_ITEMS;
+constexpr int64_t kNoSplitRows = 1024;
 
 int dw_split_rows(int64_t S, int N, int K)
 {
     using C = DwCfg;
+    // A launch this short has no reduction long enough to be worth cutting
+    // (at most four chunks of 256 rows); without a split the reduce launch
+    // is not needed either (a decode step's dW: 4.4 us saved).
+    if (S <= kNoSplitRows)
+        return 0;
     const int64_t tiles = (int64_t)((N + C::BM - 1) / C::BM) * ((K + C::BN - 1) / C::BN);
     int64_t rows = (S * tiles + kSplitCus * kSplitItems - 1) / (kSplitCus * kSplitItems);
     rows = (rows + BK - 1) / BK * BK;

@@ -54,6 +54,22 @@ __device__ __forceinline__ uint64_t lanes_below()
     return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
+// The ids of a wave's chunk: step st of this lane is slot base + 64 st +
+// lane (-1 past S).  All loads are issued before any is used: one memory
+// round trip instead of one per step.
+__device__ __forceinline__ void load_chunk_ids(const int32_t *__restrict__ ids, int64_t base,
+                                               int64_t S, bool live, int (&id)[kSlotsPerWave / kWave])
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int st = 0; st < kSlotsPerWave / kWave; ++st) {
+        const int64_t s = base + st * kWave + lane;
+        id[st] = live ? ids[min(s, S - 1)] : -1;
+        if (!live || s >= S)
+            id[st] = -1;
+    }
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t *__restrict__ ids,
                                                              int64_t S, int E, int nbits,
                                                              int nchunks, int32_t *counts,
@@ -63,15 +79,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t *__re
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int chunk = blockIdx.x * kRouteWaves + wave;
+    const int64_t base = (int64_t)chunk * kSlotsPerWave;
+    int ids_[kSlotsPerWave / kWave];
+    load_chunk_ids(ids, base, S, chunk < nchunks, ids_);
     for (int e = lane; e < E; e += kWave)
         hist[wave][e] = 0;
     __syncthreads();
     bool dropped = false;
-    const int64_t base = (int64_t)chunk * kSlotsPerWave;
+#pragma unroll
     for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
         const int64_t s = base + step * kWave + lane;
         const bool in = chunk < nchunks && s < S;
-        const int id = in ? ids[s] : -1;
+        const int id = ids_[step];
         const bool valid = in && id >= 0 && id < E;
         dropped |= in && !valid;
         const uint64_t peers = same_id_lanes(id, valid, nbits);
@@ -187,15 +206,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(const int32_t *__
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int chunk = blockIdx.x * kRouteWaves + wave;
+    const int64_t base = (int64_t)chunk * kSlotsPerWave;
+    int ids_[kSlotsPerWave / kWave];
+    load_chunk_ids(ids, base, S, chunk < nchunks, ids_);
     if (chunk < nchunks)
         for (int e = lane; e < E; e += kWave)
             cursor[wave][e] = offsets[e] + counts[(int64_t)e * nchunks + chunk];
     __syncthreads();
-    const int64_t base = (int64_t)chunk * kSlotsPerWave;
+#pragma unroll
     for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
         const int64_t s = base + step * kWave + lane;
         const bool in = chunk < nchunks && s < S;
-        const int id = in ? ids[s] : -1;
+        const int id = ids_[step];
         const bool valid = in && id >= 0 && id < E;
         const uint64_t peers = same_id_lanes(id, valid, nbits);
         const uint64_t below = peers & lanes_below();
@@ -216,14 +238,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(const int32_t *__
     }
 }
 
-// All three phases in one workgroup, for up to kSmallWaves chunks (a decode
-// step's few hundred slots): wave w counts chunk w into hist[w], the
-// workgroup turns the counts into per-chunk starts and the offsets, and wave
-// w then scatters chunk w from its cursors.  The same counting sort as the
-// three launches above, so the same bits, in one launch instead of three
-// (each a few microseconds of launch and drain on a decode step).
+// All three phases in one workgroup, for up to kSmallWaves x kSmallSteps x
+// 64 = 4096 slots (a decode step's few hundred).  The slots are cut into
+// kSmallWaves consecutive chunks of `steps` x 64 slots (steps = 1 .. 4, as
+// few as cover S, so that a small step spreads over all waves): wave w
+// counts chunk w into hist[w], the workgroup turns the counts into
+// per-chunk starts and the offsets, and wave w then scatters chunk w from
+// its cursors.  Each lane loads all its ids at once and keeps them in
+// registers for the scatter.  Chunks and lanes are in slot order, so this is
+// the same stable counting sort as the three launches above, bit for bit, in
+// one launch instead of three.
 constexpr int kSmallWaves = 16;
 constexpr int kSmallThreads = kSmallWaves * kWave;
+constexpr int kSmallSteps = 4;  // 16 measured slower on 512 slots (6.7 against 5.5 us)
+constexpr int64_t kSmallSlots = (int64_t)kSmallThreads * kSmallSteps;
 
 __global__ __launch_bounds__(kSmallThreads) void route_small(
     const int32_t *__restrict__ ids, int64_t S, int E, int nbits, int block_m, int32_t *m_sizes,
@@ -237,20 +265,30 @@ __global__ __launch_bounds__(kSmallThreads) void route_small(
     __shared__ int totals[3];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t base = (int64_t)wave * kSlotsPerWave;
+    const int steps = (int)((S + kSmallThreads - 1) / kSmallThreads);  // <= kSmallSteps
+    const int64_t base = (int64_t)wave * steps * kWave;
+    int id[kSmallSteps];
+#pragma unroll
+    for (int st = 0; st < kSmallSteps; ++st) {
+        const int64_t sl = base + st * kWave + lane;
+        id[st] = (S > 0) ? ids[min(sl, S - 1)] : -1;  // every load in flight at once
+        if (st >= steps || sl >= S)
+            id[st] = -1;
+    }
     for (int e = lane; e < E; e += kWave)
         hist[wave][e] = 0;
     __syncthreads();
     bool dropped = false;
-    for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
-        const int64_t s = base + step * kWave + lane;
-        const bool in = s < S;
-        const int id = in ? ids[s] : -1;
-        const bool valid = in && id >= 0 && id < E;
+#pragma unroll
+    for (int st = 0; st < kSmallSteps; ++st) {
+        if (st >= steps)
+            break;
+        const bool in = base + st * kWave + lane < S;
+        const bool valid = in && id[st] >= 0 && id[st] < E;
         dropped |= in && !valid;
-        const uint64_t peers = same_id_lanes(id, valid, nbits);
+        const uint64_t peers = same_id_lanes(id[st], valid, nbits);
         if (valid && (peers & lanes_below()) == 0)
-            atomicAdd(&hist[wave][id], __popcll(peers));
+            atomicAdd(&hist[wave][id[st]], __popcll(peers));
     }
     if (dropped)
         raise_error(err, kErrExpertId);
@@ -291,24 +329,27 @@ __global__ __launch_bounds__(kSmallThreads) void route_small(
     for (int64_t p = totals[0] + threadIdx.x; p < S; p += kSmallThreads)
         gather[p] = -1;  // positions left over by dropped slots
     __syncthreads();
-    for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
-        const int64_t s = base + step * kWave + lane;
-        const bool in = s < S;
-        const int id = in ? ids[s] : -1;
-        const bool valid = in && id >= 0 && id < E;
-        const uint64_t peers = same_id_lanes(id, valid, nbits);
+#pragma unroll
+    for (int st = 0; st < kSmallSteps; ++st) {
+        if (st >= steps)
+            break;
+        const int64_t sl = base + st * kWave + lane;
+        const bool in = sl < S;
+        const bool valid = in && id[st] >= 0 && id[st] < E;
+        const uint64_t peers = same_id_lanes(id[st], valid, nbits);
         const uint64_t below = peers & lanes_below();
-        const int start = valid ? hist[wave][id] : 0;
+        // All lanes read their cursor before any group leader advances it.
+        const int start = valid ? hist[wave][id[st]] : 0;
         __builtin_amdgcn_wave_barrier();
         if (valid) {
             const int pos = start + __popcll(below);
-            gather[pos] = (int32_t)s;
+            gather[pos] = (int32_t)sl;
             if (scatter)
-                scatter[s] = pos;
+                scatter[sl] = pos;
             if (below == 0)
-                hist[wave][id] = start + __popcll(peers);
+                hist[wave][id[st]] = start + __popcll(peers);
         } else if (in && scatter) {
-            scatter[s] = -1;
+            scatter[sl] = -1;
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -370,7 +411,7 @@ hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32
     const int nchunks = (int)route_chunks(S);
     const int nbits = bits_for(E);
     const int blocks = (nchunks + kRouteWaves - 1) / kRouteWaves;
-    if (nchunks <= kSmallWaves) {
+    if (S <= kSmallSlots) {
         hipLaunchKernelGGL(route_small, dim3(1), dim3(kSmallThreads), 0, stream, ids, S, E, nbits,
                            block_m, m_sizes, offsets, padded_offsets, tile_offsets, gather,
                            scatter, err);

@@ -14,11 +14,12 @@
 //      adds the group's popcount to a wave-private LDS histogram, so there is
 //      one LDS update per (expert, 64 slots) instead of one per slot.  Counts
 //      go to workspace as counts[e][chunk] (expert-major).
-//   2. route_scan (one workgroup): each wave scans whole experts' chunk rows
-//      with wave shuffles, turning counts[e][c] into the number of expert-e
-//      slots in chunks before c; then wave 0 scans the per-expert totals into
-//      offsets, padded offsets and tile offsets.
-//   3. route_scatter: each wave starts a per-expert cursor at
+//   2. route_scan: one wave per expert turns its row counts[e][c] into the
+//      number of expert-e slots in chunks before c (wave shuffles, all loads
+//      of a batch in flight at once) and writes the expert's total, m_sizes[e].
+//   3. route_scatter: every workgroup scans m_sizes over the experts in LDS
+//      (the offsets; workgroup 0 also writes them out with the padded and
+//      tile offsets), then each wave starts a per-expert cursor at
 //      offsets[e] + counts[e][chunk] and walks its chunk 64 slots at a time;
 //      a slot's position is its cursor plus the number of lower lanes with
 //      the same expert.  Chunks are in slot order and lanes are in slot
@@ -34,7 +35,7 @@ namespace moegg {
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kSlotsPerWave = 256;
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;  // one expert row per wave
 
 // Lanes (of the active, valid ones) that hold the same id as this lane.
 __device__ __forceinline__ uint64_t same_id_lanes(int id, bool valid, int nbits)
@@ -106,112 +107,105 @@ __global__ __launch_bounds__(kRouteThreads) void route_count(const int32_t *__re
 }
 
 __global__ __launch_bounds__(kScanThreads) void route_scan(int32_t *counts, int nchunks, int E,
-                                                           int block_m, int64_t S,
-                                                           int32_t *m_sizes, int32_t *offsets,
-                                                           int32_t *padded_offsets,
-                                                           int32_t *tile_offsets,
-                                                           int32_t *gather)
+                                                           int32_t *m_sizes)
 {
-    __shared__ int tot[kMaxExperts];
-    __shared__ int off[kMaxExperts];
-    __shared__ int poff[kMaxExperts];
-    __shared__ int toff[kMaxExperts];
-    __shared__ int totals[3];
-    const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
-    constexpr int kWaves = kScanThreads / kWave;
-    // Each wave scans kRows experts' chunk rows at a time; a lane owns 4
-    // consecutive chunks of each row.  All loads of a batch are issued
-    // before any is used, so a batch costs one memory round trip.
-    constexpr int kRows = 4, kPer = 4;
-    for (int e0 = wave * kRows; e0 < E; e0 += kWaves * kRows) {
-        int carry[kRows] = {0, 0, 0, 0};
-        for (int c0 = 0; c0 < nchunks; c0 += kWave * kPer) {
-            int v[kRows][kPer];
+    const int e = blockIdx.x * (kScanThreads / kWave) + threadIdx.x / kWave;
+    if (e >= E)
+        return;
+    // A lane owns kPer consecutive chunks of each batch; all loads of a batch
+    // are issued before any is used, so a batch costs one memory round trip.
+    constexpr int kPer = 8;
+    int32_t *const row = counts + (int64_t)e * nchunks;
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += kWave * kPer) {
+        int v[kPer];
 #pragma unroll
-            for (int r = 0; r < kRows; ++r)
-#pragma unroll
-                for (int q = 0; q < kPer; ++q) {
-                    const int e = e0 + r, c = c0 + lane * kPer + q;
-                    v[r][q] = (e < E && c < nchunks) ? counts[(int64_t)e * nchunks + c] : 0;
-                }
-#pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                int local = 0;
-#pragma unroll
-                for (int q = 0; q < kPer; ++q)
-                    local += v[r][q];
-                int incl = local;
-                for (int d = 1; d < kWave; d <<= 1) {
-                    const int u = __shfl_up(incl, d, kWave);
-                    if (lane >= d)
-                        incl += u;
-                }
-                int run = carry[r] + incl - local;
-                const int e = e0 + r;
-#pragma unroll
-                for (int q = 0; q < kPer; ++q) {
-                    const int c = c0 + lane * kPer + q;
-                    if (e < E && c < nchunks)
-                        counts[(int64_t)e * nchunks + c] = run;
-                    run += v[r][q];
-                }
-                carry[r] += __shfl(incl, kWave - 1, kWave);
-            }
+        for (int q = 0; q < kPer; ++q) {
+            const int c = c0 + lane * kPer + q;
+            v[q] = c < nchunks ? row[c] : 0;
         }
-        if (lane == 0)
+        int local = 0;
 #pragma unroll
-            for (int r = 0; r < kRows; ++r)
-                if (e0 + r < E)
-                    tot[e0 + r] = carry[r];
+        for (int q = 0; q < kPer; ++q)
+            local += v[q];
+        int incl = local;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int u = __shfl_up(incl, d, kWave);
+            if (lane >= d)
+                incl += u;
+        }
+        int run = carry + incl - local;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const int c = c0 + lane * kPer + q;
+            if (c < nchunks)
+                row[c] = run;
+            run += v[q];
+        }
+        carry += __shfl(incl, kWave - 1, kWave);
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kScanThreads) {
-        const int tiles = (tot[e] + block_m - 1) / block_m;
-        off[e] = tot[e];
-        poff[e] = tiles * block_m;
-        toff[e] = tiles;
-    }
-    wave0_exclusive_scan(off, E, &totals[0]);
-    wave0_exclusive_scan(poff, E, &totals[1]);
-    wave0_exclusive_scan(toff, E, &totals[2]);
-    for (int e = threadIdx.x; e < E; e += kScanThreads) {
-        m_sizes[e] = tot[e];
-        offsets[e] = off[e];
-        if (padded_offsets)
-            padded_offsets[e] = poff[e];
-        if (tile_offsets)
-            tile_offsets[e] = toff[e];
-    }
-    if (threadIdx.x == 0) {
-        offsets[E] = totals[0];
-        if (padded_offsets)
-            padded_offsets[E] = totals[1];
-        if (tile_offsets)
-            tile_offsets[E] = totals[2];
-    }
-    // Positions left over by dropped slots hold -1.
-    for (int64_t p = totals[0] + threadIdx.x; p < S; p += kScanThreads)
-        gather[p] = -1;
+    if (lane == 0)
+        m_sizes[e] = carry;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_scatter(const int32_t *__restrict__ ids,
-                                                               int64_t S, int E, int nbits,
-                                                               int nchunks,
-                                                               const int32_t *__restrict__ counts,
-                                                               const int32_t *__restrict__ offsets,
-                                                               int32_t *gather, int32_t *scatter)
+__global__ __launch_bounds__(kRouteThreads) void route_scatter(
+    const int32_t *__restrict__ ids, int64_t S, int E, int nbits, int nchunks, int block_m,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ m_sizes, int32_t *offsets,
+    int32_t *padded_offsets, int32_t *tile_offsets, int32_t *gather, int32_t *scatter)
 {
     __shared__ int cursor[kRouteWaves][kMaxExperts];
     const int wave = threadIdx.x / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int chunk = blockIdx.x * kRouteWaves + wave;
     const int64_t base = (int64_t)chunk * kSlotsPerWave;
+    __shared__ int off[kMaxExperts];
+    __shared__ int totals[3];
     int ids_[kSlotsPerWave / kWave];
     load_chunk_ids(ids, base, S, chunk < nchunks, ids_);
+    for (int e = threadIdx.x; e < E; e += kRouteThreads)
+        off[e] = m_sizes[e];
     if (chunk < nchunks)
         for (int e = lane; e < E; e += kWave)
-            cursor[wave][e] = offsets[e] + counts[(int64_t)e * nchunks + chunk];
+            cursor[wave][e] = counts[(int64_t)e * nchunks + chunk];
+    if (blockIdx.x == 0) {
+        // Workgroup 0 also writes out the padded and tile offsets.
+        __shared__ int poff[kMaxExperts];
+        __shared__ int toff[kMaxExperts];
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+            const int tiles = (off[e] + block_m - 1) / block_m;
+            poff[e] = tiles * block_m;
+            toff[e] = tiles;
+        }
+        wave0_exclusive_scan(poff, E, &totals[1]);
+        wave0_exclusive_scan(toff, E, &totals[2]);
+        for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+            if (padded_offsets)
+                padded_offsets[e] = poff[e];
+            if (tile_offsets)
+                tile_offsets[e] = toff[e];
+        }
+    }
+    wave0_exclusive_scan(off, E, &totals[0]);
+    if (blockIdx.x == 0) {
+        for (int e = threadIdx.x; e < E; e += kRouteThreads)
+            offsets[e] = off[e];
+        if (threadIdx.x == 0) {
+            offsets[E] = totals[0];
+            if (padded_offsets)
+                padded_offsets[E] = totals[1];
+            if (tile_offsets)
+                tile_offsets[E] = totals[2];
+        }
+    }
+    // Positions left over by dropped slots hold -1.
+    for (int64_t p = totals[0] + (int64_t)blockIdx.x * kRouteThreads + threadIdx.x; p < S;
+         p += (int64_t)gridDim.x * kRouteThreads)
+        gather[p] = -1;
+    if (chunk < nchunks)
+        for (int e = lane; e < E; e += kWave)
+            cursor[wave][e] += off[e];
     __syncthreads();
 #pragma unroll
     for (int step = 0; step < kSlotsPerWave / kWave; ++step) {
@@ -421,12 +415,11 @@ hipError_t route_launch(const int32_t *ids, int64_t S, int E, int block_m, int32
         hipLaunchKernelGGL(route_count, dim3(blocks), dim3(kRouteThreads), 0, stream, ids, S, E,
                            nbits, nchunks, counts, err);
     }
-    hipLaunchKernelGGL(route_scan, dim3(1), dim3(kScanThreads), 0, stream, counts, nchunks, E,
-                       block_m, S, m_sizes, offsets, padded_offsets, tile_offsets, gather);
-    if (nchunks > 0) {
-        hipLaunchKernelGGL(route_scatter, dim3(blocks), dim3(kRouteThreads), 0, stream, ids, S, E,
-                           nbits, nchunks, counts, offsets, gather, scatter);
-    }
+    hipLaunchKernelGGL(route_scan, dim3((E + kScanThreads / kWave - 1) / (kScanThreads / kWave)),
+                       dim3(kScanThreads), 0, stream, counts, nchunks, E, m_sizes);
+    hipLaunchKernelGGL(route_scatter, dim3(blocks), dim3(kRouteThreads), 0, stream, ids, S, E,
+                       nbits, nchunks, block_m, counts, m_sizes, offsets, padded_offsets,
+                       tile_offsets, gather, scatter);
     return hipGetLastError();
 }
 

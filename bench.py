@@ -526,6 +526,7 @@ def copy_calibration(nbytes=1 << 30, reps=5):
 
 KERNEL_LABELS = (("combine_fwd_kernel", "combine"), ("combine_bwd_kernel", "combine_bwd"),
                  ("fwd_kernel", "fwd"), ("dx_kernel", "dX"), ("dw_kernel", "dW"),
+                 ("dw_small_kernel", "dW"),
                  ("dw_reduce_kernel", "dW_reduce"), ("gather_x_kernel", "dW_gather"),
                  ("tail_reduce_kernel", "tail_reduce"),
                  ("groups_kernel", "groups"), ("route_count", "route_count"),

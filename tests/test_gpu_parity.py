@@ -273,6 +273,7 @@ BWD_SMALL = [
     (700, 136, 520, 6, 3, 12, (0,)),
     (33, 64, 136, 40, 8, 13, (1, 5, 39)),   # avg 6 rows/expert -> small-M dX tiles
     (100, 200, 264, 24, 4, 15, (3,)),        # small-M dX tiles with K and N tails
+    (520, 200, 264, 5, 2, 16, (1,)),         # 1040 slots: dW on the tile engine, with tails
 ]
 
 
@@ -406,6 +407,79 @@ def test_edge_shapes(mg, flags, case):
     _assert_close(gdw, rdw, f"dW {case} flags={flags}")
     for e in np.nonzero(ref_route["m_sizes"] == 0)[0][:64]:
         assert torch.count_nonzero(dW[int(e)]).item() == 0
+
+
+# dW of launches with at most 1024 slots and 16 rows per expert on average
+# runs the short-reduction kernel (64 x 64 tiles per wave, fragments loaded
+# straight from global memory): N and K tails inside a 64-wide tile and past
+# a 32-wide fragment, empty experts, and the 1024-slot boundary.
+DW_SHORT = [
+    # T, K, N, E, topk, seed, empty
+    (128, 200, 136, 64, 8, 31, (1, 5, 60)),   # 1024 slots, avg 16 rows/expert
+    (33, 72, 264, 40, 8, 32, (0, 7)),         # 264 slots, K = 64 + 8, N = 4 x 64 + 8
+    (3, 64, 64, 9, 3, 34, (4,)),              # 9 slots over 9 experts
+]
+
+
+@pytest.mark.parametrize("flags", [0, PX, PY], ids=["plain", "px", "py"])
+@pytest.mark.parametrize("case", DW_SHORT, ids=[f"T{c[0]}K{c[1]}N{c[2]}E{c[3]}k{c[4]}" for c in DW_SHORT])
+def test_dw_short_reduction(mg, flags, case):
+    T, K, N, E, topk, seed, empty = case
+    assert T * topk <= 1024
+    wl = synth.random_case(T, K, N, E, topk, flags, seed, empty=empty, with_dy=True)
+    _, _, gdw, rdw, dW, ref_route = _bwd_case(mg, wl, flags)
+    _assert_close(gdw, rdw, f"dW {case} flags={flags}")
+    for e in np.nonzero(ref_route["m_sizes"] == 0)[0]:
+        assert torch.count_nonzero(dW[int(e)]).item() == 0
+
+
+@pytest.mark.parametrize("flags", [PX, PY], ids=["px", "py"])
+def test_dw_short_reduction_zipf(mg, flags):
+    """Zipf(1.2) routing of 128 tokens over 64 experts, top-8: a hot expert
+    of 126 rows (eight sixteen-row steps, the last one partial) beside
+    experts of one or two rows and empty ones, all in one short launch."""
+    wl = synth._fine("zipf_short", 128, 200, 136, 64, 8, 1.2, 36, 36, True)
+    wl.flags = flags
+    _, _, gdw, rdw, dW, ref_route = _bwd_case(mg, wl, flags)
+    assert ref_route["m_sizes"].max() == 126
+    _assert_close(gdw, rdw, f"dW zipf flags={flags}")
+    for e in np.nonzero(ref_route["m_sizes"] == 0)[0]:
+        assert torch.count_nonzero(dW[int(e)]).item() == 0
+
+
+@pytest.mark.parametrize("flags", [PX, PY], ids=["px", "py"])
+def test_dw_short_reduction_bad_gather(mg, flags):
+    """A gather entry outside [0, S) drops its slot's term from dW and sets
+    the gather error bit.  Expected: the oracle with that slot's other
+    operand row (dY under permute_x, X under permute_y) zeroed instead."""
+    wl = synth.random_case(16, 72, 136, 16, 8, flags, 37, with_dy=True)
+    S, E = wl.S, wl.E
+    route = oracle.route(wl.ids.numpy().reshape(-1), E, 128)
+    bad_p = 5
+    gather = torch.from_numpy(route["gather"].copy())
+    gather[bad_p] = S + 7
+    X, dY = wl.X.clone(), wl.dY.clone()
+    if flags & PX:
+        dY[bad_p] = 0
+    else:
+        X[bad_p] = 0
+    ref = oracle.grouped_gemm_dW(synth.bits(X), synth.bits(dY), route["m_sizes"],
+                                 route["gather"], wl.topk, flags, E)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dW = mg.grouped_gemm_dW(_dev(wl.X), _dev(wl.dY), _dev(torch.from_numpy(route["m_sizes"])),
+                            _dev(gather), wl.topk, flags, error_flags=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & mg.DERR_GATHER
+    _assert_close(dW.reshape(E * wl.N, wl.K).float().cpu().numpy(), ref, "dW bad gather")
+
+
+def test_dw_short_reduction_fp32_out(mg):
+    wl = synth.random_case(100, 200, 136, 32, 4, PY, 35, empty=(3,), with_dy=True)
+    _, _, gdw, rdw, dW, _ = _bwd_case(mg, wl, PY, dw_flags_extra=mg.DW_FP32_OUT)
+    assert dW.dtype == torch.float32
+    ok, info = bf16_tolerance_ok(gdw, rdw, rel_fro_max=1e-5, max_elem=1e-4)
+    assert ok, info
+    assert torch.count_nonzero(dW[3]).item() == 0
 
 
 def test_dw_fp32_out(mg):

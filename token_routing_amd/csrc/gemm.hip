@@ -2030,6 +2030,180 @@ template __global__ void dx_kernel<DxSmallCfg>(DxParams);
 template __global__ void dw_kernel<DwCfg, false, false>(DwParams);
 template __global__ void dw_kernel<DwCfg, true, false>(DwParams);
 template __global__ void dw_kernel<DwCfg, false, true>(DwParams);
+
+// ---------------------------------------------------------------------------
+// dW for short reductions (a decode step: a few hundred slots spread over
+// many experts, most of them a handful of rows).  There the output is all
+// that costs (E*N*K*2 bytes against S*(N+K)*2 of operands), and the tile
+// engine spends a copy round trip and a 128 KiB LDS staging pass on every
+// 256 x 256 tile whatever its reduction length, with one workgroup per CU to
+// hide them.  Here every wave owns 64 (N) x 64 (K) output tiles and works
+// alone (no workgroup barrier after the expert table):
+//   * operands come from global memory straight into MFMA fragments.  Lane
+//     l of v_mfma_f32_32x32x16_bf16 needs 8 consecutive reduction rows of one
+//     column: 8 two-byte buffer loads per fragment (32 lanes read 64
+//     contiguous bytes of one row; rows past the expert read zero), rows
+//     gathered under permute_x / permute_y.  The operands are a few MB and
+//     stay in L2.
+//   * the tile is computed as its transpose (MFMA rows along K), so a lane
+//     holds 4 consecutive K values of one N row; it is rounded to bf16 into
+//     a wave-private LDS tile and written out as whole 128-byte row segments,
+//     8 rows per store instruction (fp32 output is stored from the
+//     accumulators, 16 bytes per lane).
+//   * an empty expert's tiles are zeros through the same path.
+// Tiles are dealt round-robin over the waves (eight per CU).  The stores
+// bound it: on the decode step the same launch with every expert empty (no
+// loads, no MFMAs) takes as long as the real one.
+constexpr int kSdwWaves = 4;  // waves per workgroup
+constexpr int kSdwT = 64;     // output tile: kSdwT rows of N by kSdwT columns of K
+constexpr uint32_t kSdwOOB = 1u << 30;
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+
+template <bool PX, bool PY>
+__global__ __launch_bounds__(kSdwWaves * kWave) void dw_small_kernel(DwParams a)
+{
+    __shared__ int s_roff[kMaxExperts + 1];
+    __shared__ int s_scratch[2];
+    __shared__ __attribute__((aligned(16))) char s_out[kSdwWaves][kSdwT * kSdwT * 2];
+    static_assert(sizeof(s_out) >= (kMaxExperts + 1) * sizeof(int), "tile table fits");
+    // The table's tile starts are not used here: they go to the output tiles'
+    // LDS (four workgroups per CU fit), which the barrier at its end frees.
+    build_expert_tables(a.m_sizes, a.E, a.S, s_roff, reinterpret_cast<int *>(&s_out[0][0]),
+                        s_scratch, a.err, [](int) { return 0; });
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+    const int col = lane & 31, half = lane >> 5;
+    const int ntn = (a.N + kSdwT - 1) / kSdwT, ntk = (a.K + kSdwT - 1) / kSdwT;
+    const int per_expert = ntn * ntk;
+    const int64_t total = (int64_t)per_expert * a.E;
+    const bool f32out = a.flags & MOEGG_DW_FP32_OUT;
+    // Operands below 1 GiB each (checked on the host): offsets of 1 GiB and
+    // above (kSdwOOB, alone or added to a row or column offset) read zero.
+    const uint32_t xrow = (uint32_t)a.K * 2, yrow = (uint32_t)a.N * 2;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(a.X), 0, (int)((PX ? a.S / a.topk : a.S) * xrow), 0x00020000);
+    const __amdgpu_buffer_rsrc_t yr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(a.dY), 0, (int)(a.S * yrow), 0x00020000);
+    char *const lds = s_out[wave];
+    const uint32_t Su = (uint32_t)a.S;
+    bool bad = false;
+    // Byte offsets of this lane's 8 reduction rows c0 + 8 * half + i of the
+    // expert starting at slot `start`, in X and in dY (kSdwOOB: zeros, past
+    // the expert or a bad gather entry).  The gather loads are unconditional,
+    // from clamped in-bounds addresses, so all 8 are in flight together.
+    auto step_rows = [&](int start, int m_e, int c0, uint32_t (&ox)[8], uint32_t (&oy)[8]) {
+        int g[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int p = start + min(c0 + 8 * half + i, m_e - 1);
+            g[i] = (PX || PY) ? a.gather[p] : p;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int m = c0 + 8 * half + i, p = start + m;
+            const bool in = m < m_e;
+            const bool ok = !(PX || PY) || (uint32_t)g[i] < Su;
+            bad |= in && !ok;
+            const int rx = !PX ? p : fast_div((uint32_t)g[i], a.topk_div);
+            const int ry = !PY ? p : g[i];
+            ox[i] = in && (ok || !PX) ? (uint32_t)rx * xrow : kSdwOOB;
+            oy[i] = in && (ok || !PY) ? (uint32_t)ry * yrow : kSdwOOB;
+        }
+    };
+    // Fragment of column c (< lim) over the 8 rows at byte offsets off[]:
+    // buffer loads, so that an offset past the operand reads zero.
+    auto frag = [&](__amdgpu_buffer_rsrc_t r, const uint32_t (&off)[8], int c,
+                    int lim) -> bf16x8_t {
+        const uint32_t co = c < lim ? (uint32_t)c * 2 : kSdwOOB;
+        u16x8_t v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = __builtin_amdgcn_raw_buffer_load_b16(r, off[i] + co, 0, 0);
+        return __builtin_bit_cast(bf16x8_t, v);
+    };
+    // Tiles are dealt out round-robin over the waves (an expert's tiles cost
+    // in proportion to its rows, so contiguous runs would leave the waves
+    // of a hot expert behind the rest).
+    const int64_t nwaves = (int64_t)gridDim.x * kSdwWaves;
+    for (int64_t t = (int64_t)xcd_logical_block(blockIdx.x, gridDim.x) * kSdwWaves + wave;
+         t < total; t += nwaves) {
+        const int e = (int)(t / per_expert), u = (int)(t % per_expert);
+        const int n0 = (u / ntk) * kSdwT, k0 = (u % ntk) * kSdwT;
+        const int start = s_roff[e], m_e = s_roff[e + 1] - start;
+        f32x16_t acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+        for (int c0 = 0; c0 < m_e; c0 += 16) {
+            uint32_t ox[8], oy[8];
+            step_rows(start, m_e, c0, ox, oy);
+            bf16x8_t fa[2], fb[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                fa[j] = frag(xr, ox, k0 + 32 * j + col, a.K);
+                fb[j] = frag(yr, oy, n0 + 32 * j + col, a.N);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
+                                                                         0, 0, 0);
+        }
+        // acc[i][j][r]: K column k0 + 32 i + 8 (r / 4) + 4 half + r % 4 of
+        // N row n0 + 32 j + col.
+        if (f32out) {
+            float *const out = reinterpret_cast<float *>(a.dW);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int n = n0 + 32 * j + col, k = k0 + 32 * i + 8 * g + 4 * half;
+                        if (n < a.N && k < a.K) {
+                            const float4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                              acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                            *reinterpret_cast<float4 *>(out + ((int64_t)e * a.N + n) * a.K + k) = v;
+                        }
+                    }
+            continue;
+        }
+        wait_lds();  // the previous tile's reads of this wave's LDS tile are done
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = 32 * j + col;
+                    const uint2 v = {pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]),
+                                     pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                    *reinterpret_cast<uint2 *>(lds + row * (kSdwT * 2) +
+                                               swz_chunk(row, 4 * i + g) * 16 + half * 8) = v;
+                }
+        wait_lds();  // every lane's writes are in LDS before any lane reads them
+        char *const base = a.dW + (((int64_t)e * a.N + n0) * a.K + k0) * 2;
+#pragma unroll
+        for (int q = 0; q < kSdwT * kSdwT * 2 / 16 / kWave; ++q) {
+            const int idx = q * kWave + lane;
+            const int row = idx / 8, c = idx % 8;
+            const u32x4_nt_t v = *reinterpret_cast<const u32x4_nt_t *>(
+                lds + row * (kSdwT * 2) + swz_chunk(row, c) * 16);
+            if (n0 + row < a.N && k0 + 8 * c < a.K)
+                __builtin_nontemporal_store(
+                    v, reinterpret_cast<u32x4_nt_t *>(base + ((int64_t)row * a.K + 8 * c) * 2));
+        }
+    }
+    if (bad)
+        raise_error(a.err, kErrGather);
+}
+template __global__ void dw_small_kernel<false, false>(DwParams);
+template __global__ void dw_small_kernel<true, false>(DwParams);
+template __global__ void dw_small_kernel<false, true>(DwParams);
 template __global__ void groups_kernel<GroupCfg, true>(GroupsParams);
 template __global__ void groups_kernel<GroupCfg, false>(GroupsParams);
 
@@ -2162,10 +2336,7 @@ hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 // left with one hot expert's whole reduction.  An expert splits only if it
 // has more rows than that; a split expert has fewer than 2 m / split_rows
 // chunks, so all of them together hold fewer than 2 S / split_rows partials.
-#ifndef MOEGG_DW_SPLIT_ITEMS
-#define MOEGG_DW_SPLIT_ITEMS 3
-#endif
-constexpr int kSplitCus = 256, kSplitItems = MOEGG_DW_SPLIT_ITEMS;
+constexpr int kSplitCus = 256, kSplitItems = 3;
 constexpr int64_t kNoSplitRows = 1024;
 
 int dw_split_rows(int64_t S, int N, int K)
@@ -2257,9 +2428,41 @@ static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 }
 
 
+// Launches of at most 1024 slots and at most 16 rows per expert on average
+// take dw_small_kernel (no split, no gather copy: the rows are gathered as
+// the fragments are loaded).  Measured on MI355X, 128 experts of 2048 x 768:
+// a 64-token top-8 decode step (512 slots) 0.092 -> 0.080 ms; 64 experts of
+// 2048 x 1408, 512 slots 0.082 -> 0.071 ms; 64 experts of 2048 x 768, 1024
+// slots 0.052 -> 0.049 ms.  With 128 rows per expert (8 experts of
+// 4096 x 4096, 1024 slots) it is 2.3x slower than the tile engine, whose
+// cost does not grow with the reduction here.
+constexpr int64_t kSmallDwSlots = 1024, kSmallDwRowsPerExpert = 16;
+
+template <bool PX, bool PY>
+static void dw_small_launch(const DwParams &p, int cus, hipStream_t stream)
+{
+    const int64_t tiles = (int64_t)p.E * ((p.N + kSdwT - 1) / kSdwT) * ((p.K + kSdwT - 1) / kSdwT);
+    static int res = resident_blocks(dw_small_kernel<PX, PY>, kSdwWaves * kWave);
+    hipLaunchKernelGGL((dw_small_kernel<PX, PY>),
+                       dim3(grid_for((tiles + kSdwWaves - 1) / kSdwWaves, cus, res)),
+                       dim3(kSdwWaves * kWave), 0, stream, p);
+}
+
 hipError_t dw_launch(const DwParams &pin, int cus, hipStream_t stream)
 {
     DwParams p = pin;
+    const int64_t x_rows = (p.flags & MOEGG_PERMUTE_X) ? p.S / p.topk : p.S;
+    if (p.S <= kSmallDwSlots && p.S <= kSmallDwRowsPerExpert * p.E &&
+        p.S * p.N * 2 < (int64_t)kSdwOOB &&
+        x_rows * p.K * 2 < (int64_t)kSdwOOB) {
+        if (p.flags & MOEGG_PERMUTE_X)
+            dw_small_launch<true, false>(p, cus, stream);
+        else if (p.flags & MOEGG_PERMUTE_Y)
+            dw_small_launch<false, true>(p, cus, stream);
+        else
+            dw_small_launch<false, false>(p, cus, stream);
+        return hipGetLastError();
+    }
     if (p.xg && (p.flags & MOEGG_PERMUTE_X) && p.S > 0) {
         hipLaunchKernelGGL(gather_x_kernel, dim3((unsigned)std::min<int64_t>(p.S, (int64_t)cus * 16)),
                            dim3(256), 0, stream, p);

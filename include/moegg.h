@@ -238,6 +238,10 @@ size_t moegg_grouped_gemm_dX_workspace_bytes(int32_t num_tokens, int32_t topk,
  * dW is [E, N, K], bf16, or fp32 with MOEGG_DW_FP32_OUT.  Experts with no
  * rows get exact zeros.
  *
+ * Short launches (S <= 1024 and S <= 16 * num_experts, each operand below
+ * 1 GiB, e.g. a decode step) run a kernel whose cost is its output stores:
+ * no split and no gather copy, so any workspace is left unused.
+ *
  * Split reduction (the split-k of triton_kernels/matmul_ogs.py, whose fp32
  * partials a separate reduce sums, applied to the rows of hot experts):
  * with a workspace, an expert holding many more rows than the average is
@@ -281,9 +285,10 @@ size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
  * outside [0, S); positions past the sum of m_sizes, where routing leaves
  * its dropped slots, are read by neither.  On MI355X the copy plus the
  * reduction take less time.  The copy is an operand like X and must stay
- * below 2 GiB: when S * K * 2 >= 2^31 this returns
- * moegg_grouped_gemm_dW_workspace_bytes(...) and moegg_grouped_gemm_dW
- * gathers inside the reduction whatever the workspace size.  A workspace of
+ * below 2 GiB: when S * K * 2 >= 2^31, or for a short launch (see
+ * moegg_grouped_gemm_dW), this returns moegg_grouped_gemm_dW_workspace_bytes(...)
+ * and moegg_grouped_gemm_dW gathers inside the reduction whatever the
+ * workspace size.  A workspace of
  * at least moegg_grouped_gemm_dW_workspace_bytes(...) bytes but less than
  * this keeps the gather inside the reduction.  Without MOEGG_PERMUTE_X the
  * extra bytes are unused.

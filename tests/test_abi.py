@@ -137,6 +137,11 @@ def test_dw_gather_copy_size_rule(lib):
         g, w = both(T, 8, 4, 64, 8192)
         assert T * 8192 * 2 < 2 ** 31 <= T * 8 * 8192 * 2
         assert g == w and w > 0
+    # a short launch (S <= 1024 and S <= 16 E) never copies
+    assert both(64, 8, 128, 2048, 768) == (0, 0)
+    assert both(64, 8, 32, 2048, 768) == (0, 0)
+    g, w = both(64, 8, 31, 2048, 768)          # 512 slots > 16 x 31
+    assert w == 0 and g == 512 * 768 * 2
 
 
 def test_operand_size_limit(lib):

@@ -594,7 +594,7 @@ def test_host_validation_statuses(mg):
 # the split area, so hot experts are cut into the same chunks) the sums are
 # the same in the same order, so the two agree bit for bit; the copy path is
 # also checked against the oracle.
-DW_GATHERED = [(300, 72, 264, 4, 2, 21), (1100, 136, 136, 3, 2, 22), (37, 264, 72, 8, 3, 23)]
+DW_GATHERED = [(300, 72, 264, 4, 2, 21), (1100, 136, 136, 3, 2, 22), (37, 264, 72, 4, 3, 23)]
 
 
 @pytest.mark.parametrize("T,N,K,E,topk,seed", DW_GATHERED)

@@ -344,7 +344,8 @@ size_t moegg_grouped_gemm_dW_gather_workspace_bytes(int32_t num_tokens, int32_t 
     if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
         return 0;
     const int64_t S = (int64_t)num_tokens * topk;
-    if (!fits(S, K))  // no copy: the rows are gathered inside the reduction
+    // No copy: the rows are gathered inside the reduction.
+    if (!fits(S, K) || moegg::dw_short_launch(S, num_tokens, num_experts, N, K))
         return (size_t)moegg::dw_workspace_bytes(S, num_experts, N, K);
     return (size_t)(moegg::dw_gather_offset(S, num_experts, N, K) + S * K * 2);
 }

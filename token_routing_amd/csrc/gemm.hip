@@ -2438,6 +2438,12 @@ static void dw_launch_flags(const DwParams &p, int cus, hipStream_t stream)
 // cost does not grow with the reduction here.
 constexpr int64_t kSmallDwSlots = 1024, kSmallDwRowsPerExpert = 16;
 
+bool dw_short_launch(int64_t S, int64_t x_rows, int E, int N, int K)
+{
+    return S <= kSmallDwSlots && S <= kSmallDwRowsPerExpert * E &&
+           S * N * 2 < (int64_t)kSdwOOB && x_rows * K * 2 < (int64_t)kSdwOOB;
+}
+
 template <bool PX, bool PY>
 static void dw_small_launch(const DwParams &p, int cus, hipStream_t stream)
 {
@@ -2451,10 +2457,7 @@ static void dw_small_launch(const DwParams &p, int cus, hipStream_t stream)
 hipError_t dw_launch(const DwParams &pin, int cus, hipStream_t stream)
 {
     DwParams p = pin;
-    const int64_t x_rows = (p.flags & MOEGG_PERMUTE_X) ? p.S / p.topk : p.S;
-    if (p.S <= kSmallDwSlots && p.S <= kSmallDwRowsPerExpert * p.E &&
-        p.S * p.N * 2 < (int64_t)kSdwOOB &&
-        x_rows * p.K * 2 < (int64_t)kSdwOOB) {
+    if (dw_short_launch(p.S, (p.flags & MOEGG_PERMUTE_X) ? p.S / p.topk : p.S, p.E, p.N, p.K)) {
         if (p.flags & MOEGG_PERMUTE_X)
             dw_small_launch<true, false>(p, cus, stream);
         else if (p.flags & MOEGG_PERMUTE_Y)

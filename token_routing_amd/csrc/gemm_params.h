@@ -136,6 +136,9 @@ hipError_t fwd_launch(const FwdParams &p, int cus, hipStream_t stream);
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream);
 int64_t dx_workspace_bytes(int64_t S, int E, int N, int K, int cus);
 hipError_t dw_launch(const DwParams &p, int cus, hipStream_t stream);
+// True when dw_launch takes the short-reduction kernel for S slots (X with
+// x_rows rows): no split and no gather copy, so no workspace is used.
+bool dw_short_launch(int64_t S, int64_t x_rows, int E, int N, int K);
 
 // Split plan sizes: rows per chunk for a launch of S rows (0: no expert can
 // split), the header size and the whole workspace (0 when no split is possible).

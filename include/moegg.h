@@ -10,8 +10,13 @@
  *   the j-th expert choice of token t (row-major [T, k] order).
  *   E = num_experts.  W is [E, N, K] row-major (K contiguous), the layout of
  *   grouped_gemm_forward in unsloth grouped_gemm/interface.py.
- *   bf16 tensors are row-major, 2 bytes per element, rows 16-byte aligned:
- *   K and N must be multiples of 8 and base pointers 16-byte aligned.
+ *   bf16 tensors are row-major, 2 bytes per element; base pointers must be
+ *   2-byte aligned (fp32 outputs 4-byte).  Any K and N are accepted: when
+ *   every row of a call is whole 16-byte chunks (K and N multiples of 8 and
+ *   operands 16-byte aligned) the tiled kernels run, otherwise slower
+ *   any-shape kernels that compute the same definitions (no workspace;
+ *   workspace arguments are then ignored and the workspace size queries
+ *   return 0 for such K and N).
  *   Each input operand (X, dY, one expert's W, a group's x or w) must be
  *   smaller than 2 GiB: the kernels address them with 32-bit offsets.
  *   Index tensors are int32.  "sorted position" p indexes the expert-grouped
@@ -163,7 +168,7 @@ moegg_status moegg_route_noalloc(const int32_t *topk_ids, int32_t num_tokens, in
  *              out[c] = silu(y[2c]) * y[2c + 1],  silu(x) = x / (1 + e^-x),
  *            from the fp32 accumulators, rounded once to bf16.  Y is
  *            [S, N/2].  Not with PERMUTE_Y or FUSE_MUL_POST (the activation
- *            belongs to the first GEMM); N must be a multiple of 16.
+ *            belongs to the first GEMM); N must be even.
  *
  *   m_sizes     [E] device int32 rows per expert (moegg_route output); read
  *               on the device, no host synchronisation.
@@ -173,9 +178,9 @@ moegg_status moegg_route_noalloc(const int32_t *topk_ids, int32_t num_tokens, in
  * Errors: EINVAL if both permute flags are set, FUSE_MUL_POST without
  * PERMUTE_Y, GATED_SILU with PERMUTE_Y or FUSE_MUL_POST, an unknown flag, or
  * a required pointer is NULL (gather_idx with a permute flag, topk_weights
- * with FUSE_MUL_POST); ESHAPE for non-positive sizes, K or N not a multiple
- * of 8 (of 16 for N with GATED_SILU), E > MOEGG_MAX_EXPERTS.  T = 0 is a
- * no-op.
+ * with FUSE_MUL_POST); ESHAPE for non-positive sizes, odd N with
+ * GATED_SILU, E > MOEGG_MAX_EXPERTS, a pointer that is not 2-byte aligned.
+ * T = 0 is a no-op.
  */
 moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t *m_sizes,
                                     const int32_t *gather_idx, const float *topk_weights,
@@ -322,7 +327,7 @@ typedef struct {
  *   trans_b     0: w is [k, n]; 1: w is [n, k].  trans_a is not offered
  *               (inputs are [m, k]).
  * Errors: EINVAL for a NULL pointer or bad trans_b; ESHAPE for negative
- * sizes, n, k, ldx, ldw, ldy not multiples of 8, or a leading dimension
+ * sizes, a pointer that is not 2-byte aligned, or a leading dimension
  * smaller than its row.
  */
 moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_groups,
@@ -354,7 +359,7 @@ moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_gr
  *                  fp32.  Every element is written.
  *   error_flags    optional device int32; an entry of scatter_idx at or above
  *                  y_rows sets MOEGG_DERR_GATHER and the slot is skipped.
- * N must be a multiple of 8; Y and out 16-byte aligned.  T = 0 is a no-op.
+ * Any N; Y and out 2-byte aligned (out 4-byte for fp32).  T = 0 is a no-op.
  * Errors: ESHAPE for bad sizes, EINVAL for unknown flags, NULL or misaligned
  * pointers.
  */

@@ -76,16 +76,34 @@ def test_fwd_missing_pointers(lib):
 
 
 @pytest.mark.parametrize("T,k,E,N,K", [(-1, 2, 8, 64, 64), (10, 0, 8, 64, 64), (10, 2, 0, 64, 64),
-                                       (10, 2, 1025, 64, 64), (10, 2, 8, 60, 64),
-                                       (10, 2, 8, 64, 2), (10, 2, 8, 0, 64)])
+                                       (10, 2, 1025, 64, 64), (10, 2, 8, 0, 64),
+                                       (10, 2, 8, 64, 0)])
 def test_fwd_shape_checks(lib, T, k, E, N, K):
     assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, T, k, E, N, K, 0, FAKE, None,
                                       None) == ESHAPE
 
 
+ODD = ctypes.c_void_p((1 << 20) + 1)  # not even 2-byte aligned: never valid for bf16
+
+
+def test_misaligned_element_pointers(lib):
+    # any K and N are accepted (rows that are not whole 16-byte chunks take
+    # the any-shape kernels), but a bf16 operand must be 2-byte aligned
+    assert lib.moegg_grouped_gemm_fwd(ODD, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 60, 70, 0, FAKE,
+                                      None, None) == ESHAPE
+    assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 60, 70, 0, ODD, None, 0,
+                                     None, None) == ESHAPE
+    assert lib.moegg_grouped_gemm_dW(FAKE, ODD, FAKE, FAKE, 10, 2, 8, 60, 70, 0, FAKE, None, 0,
+                                     None, None) == ESHAPE
+    # fp32 dW needs 4-byte alignment
+    two = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.moegg_grouped_gemm_dW(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 60, 70, F32, two, None, 0,
+                                     None, None) == ESHAPE
+
+
 def test_gated_shape_and_backward_checks(lib):
-    # N/2 output columns must be whole 16-byte segments
-    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 40, 64, GS | PX,
+    # W rows come in (gate, linear) pairs: N must be even
+    assert lib.moegg_grouped_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 41, 64, GS | PX,
                                       FAKE, None, None) == ESHAPE
     # the backward kernels take no activation flag
     assert lib.moegg_grouped_gemm_dX(FAKE, FAKE, FAKE, FAKE, 10, 2, 8, 64, 64, GS, FAKE, None, 0,
@@ -178,7 +196,7 @@ def test_groups_checks(lib):
     import token_routing_amd as mg
     g = (mg.MoeggGroup * 2)()
     g[0] = mg.MoeggGroup(1 << 20, 1 << 20, 1 << 20, 16, 64, 64, 64, 64, 64)
-    g[1] = mg.MoeggGroup(1 << 20, 1 << 20, 1 << 20, 16, 60, 64, 64, 64, 64)  # n % 8 != 0
+    g[1] = mg.MoeggGroup(1 << 20, (1 << 20) + 1, 1 << 20, 16, 60, 64, 64, 64, 64)  # odd address
     assert lib.moegg_grouped_gemm_groups(g, 2, 0, None) == ESHAPE
     assert lib.moegg_grouped_gemm_groups(g, 1, 2, None) == EINVAL       # bad trans_b
     assert lib.moegg_grouped_gemm_groups(g, 0, 0, None) == ESHAPE       # no groups
@@ -189,8 +207,8 @@ def test_groups_checks(lib):
 
 def test_combine_checks(lib):
     CF32 = 16
-    # N not a multiple of 8; negative tokens; slot-order Y with too few rows
-    assert lib.moegg_combine(FAKE, None, None, 10, 2, 60, 20, 0, FAKE, None, None) == ESHAPE
+    # an odd address (any N is accepted); negative tokens; slot-order Y with too few rows
+    assert lib.moegg_combine(ODD, None, None, 10, 2, 60, 20, 0, FAKE, None, None) == EINVAL
     assert lib.moegg_combine(FAKE, None, None, -1, 2, 64, 20, 0, FAKE, None, None) == ESHAPE
     assert lib.moegg_combine(FAKE, None, None, 10, 2, 64, 19, 0, FAKE, None, None) == ESHAPE
     assert lib.moegg_combine(FAKE, None, None, 10, 0, 64, 20, 0, FAKE, None, None) == ESHAPE
@@ -202,7 +220,7 @@ def test_combine_checks(lib):
     # backward: dw needs the forward input
     assert lib.moegg_combine_bwd(FAKE, None, None, None, 10, 2, 64, 20, FAKE, FAKE, None,
                                  None) == EINVAL
-    assert lib.moegg_combine_bwd(FAKE, FAKE, None, None, 10, 2, 60, 20, FAKE, None, None,
+    assert lib.moegg_combine_bwd(FAKE, FAKE, None, None, 10, 2, 60, -1, FAKE, None, None,
                                  None) == ESHAPE
     assert lib.moegg_combine_bwd(None, None, None, None, 0, 2, 64, 0, None, None, None,
                                  None) == 0

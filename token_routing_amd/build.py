@@ -32,7 +32,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
-SOURCES = ["route.hip", "gemm.hip", "combine.hip", "api.hip"]
+SOURCES = ["route.hip", "gemm.hip", "generic.hip", "combine.hip", "api.hip"]
 
 
 def _compile(src: str, report: bool, defines=(), build_dir=BUILD) -> str:

@@ -39,11 +39,27 @@ bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// bf16 (fp32) elements need 2- (4-) byte alignment on every path.
+bool aligned2(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 1u) == 0;
+}
+bool aligned4(const void *p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
+}
+
+// The tiled kernels move rows as 16-byte chunks: row lengths that are
+// multiples of 8 elements and 16-byte aligned operands.  Other shapes take
+// the any-shape launches.
+bool tiled_rows(int64_t n, int64_t k)
+{
+    return n % 8 == 0 && k % 8 == 0;
+}
+
 moegg_status check_gemm_common(int32_t num_tokens, int32_t topk, int32_t E, int32_t N, int32_t K)
 {
     if (num_tokens < 0 || topk < 1 || E < 1 || E > MOEGG_MAX_EXPERTS || N < 1 || K < 1)
-        return MOEGG_ESHAPE;
-    if (N % 8 != 0 || K % 8 != 0)
         return MOEGG_ESHAPE;
     if ((int64_t)num_tokens * topk > INT32_MAX)
         return MOEGG_ESHAPE;
@@ -173,16 +189,18 @@ moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t 
         return MOEGG_EINVAL;  // the gate multiply is fused only with permute_y
     if ((flags & MOEGG_GATED_SILU) && (flags & (MOEGG_PERMUTE_Y | MOEGG_FUSE_MUL_POST)))
         return MOEGG_EINVAL;  // the activation belongs to the first GEMM
-    if ((flags & MOEGG_GATED_SILU) && N % 16 != 0)
-        return MOEGG_ESHAPE;  // N/2 output columns in 16-byte segments
+    if ((flags & MOEGG_GATED_SILU) && N % 2 != 0)
+        return MOEGG_ESHAPE;  // W rows come in (gate, linear) pairs
     if ((flags & MOEGG_FUSE_MUL_POST) && num_tokens > 0 && topk_weights == nullptr)
         return MOEGG_EINVAL;
     if (num_tokens == 0)
         return MOEGG_OK;
     if (X == nullptr || W == nullptr || m_sizes == nullptr || Y == nullptr)
         return MOEGG_EINVAL;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
+    if (!aligned2(X) || !aligned2(W) || !aligned2(Y))
         return MOEGG_ESHAPE;
+    const bool tiled = tiled_rows(N, K) && (!(flags & MOEGG_GATED_SILU) || N % 16 == 0) &&
+                       aligned16(X) && aligned16(W) && aligned16(Y);
     {
         const int64_t S = (int64_t)num_tokens * topk;
         const int64_t x_rows = (flags & MOEGG_PERMUTE_X) ? num_tokens : S;
@@ -206,7 +224,8 @@ moegg_status moegg_grouped_gemm_fwd(const void *X, const void *W, const int32_t 
     p.N = N;
     p.K = K;
     p.flags = flags;
-    return from_hip(moegg::fwd_launch(p, cus, static_cast<hipStream_t>(stream)));
+    return from_hip(tiled ? moegg::fwd_launch(p, cus, static_cast<hipStream_t>(stream))
+                          : moegg::fwd_any_launch(p, cus, static_cast<hipStream_t>(stream)));
 }
 
 moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t *m_sizes,
@@ -228,15 +247,16 @@ moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t 
         return MOEGG_OK;
     if (dY == nullptr || W == nullptr || m_sizes == nullptr || dX == nullptr)
         return MOEGG_EINVAL;
-    if (!aligned16(dY) || !aligned16(W) || !aligned16(dX) || !aligned16(workspace))
+    if (!aligned2(dY) || !aligned2(W) || !aligned2(dX) || !aligned16(workspace))
         return MOEGG_ESHAPE;
     if (!fits((int64_t)num_tokens * topk, N) || !fits(N, K))
         return MOEGG_ESHAPE;
+    const bool tiled = tiled_rows(N, K) && aligned16(dY) && aligned16(W) && aligned16(dX);
     int cus = 0;
     if (device_cus(&cus) != 0)
         return MOEGG_EHIP;
     const int64_t ws_need =
-        moegg::dx_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K, cus);
+        tiled ? moegg::dx_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K, cus) : 0;
     if (workspace != nullptr && (int64_t)workspace_bytes < ws_need)
         return MOEGG_EWORKSPACE;
     moegg::DxParams p;
@@ -253,7 +273,8 @@ moegg_status moegg_grouped_gemm_dX(const void *dY, const void *W, const int32_t 
     p.N = N;
     p.K = K;
     p.flags = flags;
-    return from_hip(moegg::dx_launch(p, cus, static_cast<hipStream_t>(stream)));
+    return from_hip(tiled ? moegg::dx_launch(p, cus, static_cast<hipStream_t>(stream))
+                          : moegg::dx_any_launch(p, cus, static_cast<hipStream_t>(stream)));
 }
 
 moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t *m_sizes,
@@ -275,7 +296,9 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
         return MOEGG_EINVAL;
     if (num_tokens > 0 && (X == nullptr || dY == nullptr))
         return MOEGG_EINVAL;
-    if (!aligned16(X) || !aligned16(dY) || !aligned16(dW) || !aligned16(workspace))
+    if (!aligned2(X) || !aligned2(dY) || !aligned2(dW) || !aligned16(workspace))
+        return MOEGG_ESHAPE;
+    if ((flags & MOEGG_DW_FP32_OUT) && !aligned4(dW))
         return MOEGG_ESHAPE;
     {
         const int64_t S = (int64_t)num_tokens * topk;
@@ -283,7 +306,9 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
         if (!fits(x_rows, K) || !fits(S, N))
             return MOEGG_ESHAPE;
     }
-    const int64_t ws_need = moegg::dw_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K);
+    const bool tiled = tiled_rows(N, K) && aligned16(X) && aligned16(dY) && aligned16(dW);
+    const int64_t ws_need =
+        tiled ? moegg::dw_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K) : 0;
     const bool use_ws = workspace != nullptr && ws_need > 0;
     if (workspace != nullptr && (int64_t)workspace_bytes < ws_need)
         return MOEGG_EWORKSPACE;
@@ -292,7 +317,7 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     // below 2 GiB too; a larger one keeps the gather inside the reduction.
     const int64_t xg_off = moegg::dw_gather_offset((int64_t)num_tokens * topk, num_experts, N, K);
     const int64_t xg_bytes = (int64_t)num_tokens * topk * K * 2;
-    const bool use_xg = workspace != nullptr && (flags & MOEGG_PERMUTE_X) && xg_bytes > 0 &&
+    const bool use_xg = tiled && workspace != nullptr && (flags & MOEGG_PERMUTE_X) && xg_bytes > 0 &&
                         fits((int64_t)num_tokens * topk, K) &&
                         (int64_t)workspace_bytes >= xg_off + xg_bytes;
     int cus = 0;
@@ -316,13 +341,14 @@ moegg_status moegg_grouped_gemm_dW(const void *X, const void *dY, const int32_t 
     p.ws = use_ws ? static_cast<char *>(workspace) : nullptr;
     p.xg = use_xg ? static_cast<char *>(workspace) + xg_off : nullptr;
     p.split_rows = use_ws ? moegg::dw_split_rows(p.S, N, K) : 0;
-    return from_hip(moegg::dw_launch(p, cus, static_cast<hipStream_t>(stream)));
+    return from_hip(tiled ? moegg::dw_launch(p, cus, static_cast<hipStream_t>(stream))
+                          : moegg::dw_any_launch(p, cus, static_cast<hipStream_t>(stream)));
 }
 
 size_t moegg_grouped_gemm_dX_workspace_bytes(int32_t num_tokens, int32_t topk,
                                              int32_t num_experts, int32_t N, int32_t K)
 {
-    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
+    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK || !tiled_rows(N, K))
         return 0;
     int cus = 0;
     if (device_cus(&cus) != 0)
@@ -333,7 +359,7 @@ size_t moegg_grouped_gemm_dX_workspace_bytes(int32_t num_tokens, int32_t topk,
 size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
                                              int32_t num_experts, int32_t N, int32_t K)
 {
-    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
+    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK || !tiled_rows(N, K))
         return 0;
     return (size_t)moegg::dw_workspace_bytes((int64_t)num_tokens * topk, num_experts, N, K);
 }
@@ -341,7 +367,7 @@ size_t moegg_grouped_gemm_dW_workspace_bytes(int32_t num_tokens, int32_t topk,
 size_t moegg_grouped_gemm_dW_gather_workspace_bytes(int32_t num_tokens, int32_t topk,
                                                     int32_t num_experts, int32_t N, int32_t K)
 {
-    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK)
+    if (check_gemm_common(num_tokens, topk, num_experts, N, K) != MOEGG_OK || !tiled_rows(N, K))
         return 0;
     const int64_t S = (int64_t)num_tokens * topk;
     // No copy: the rows are gathered inside the reduction.
@@ -359,19 +385,19 @@ moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_gr
         return MOEGG_ESHAPE;
     moegg::GroupsParams p;
     p.num = num_groups;
-    bool any = false;
+    bool any = false, tiled = true;
     for (int i = 0; i < num_groups; ++i) {
         const moegg_group &g = groups[i];
         if (g.m < 0 || g.n < 1 || g.k < 1)
-            return MOEGG_ESHAPE;
-        if (g.n % 8 || g.k % 8 || g.ldx % 8 || g.ldw % 8 || g.ldy % 8)
             return MOEGG_ESHAPE;
         if (g.ldx < g.k || g.ldy < g.n || g.ldw < (trans_b ? g.k : g.n))
             return MOEGG_ESHAPE;
         if (g.m > 0 && (g.x == nullptr || g.w == nullptr || g.y == nullptr))
             return MOEGG_EINVAL;
-        if (!aligned16(g.x) || !aligned16(g.w) || !aligned16(g.y))
+        if (!aligned2(g.x) || !aligned2(g.w) || !aligned2(g.y))
             return MOEGG_ESHAPE;
+        tiled &= !(g.n % 8 || g.k % 8 || g.ldx % 8 || g.ldw % 8 || g.ldy % 8) &&
+                 aligned16(g.x) && aligned16(g.w) && aligned16(g.y);
         if (!fits(g.m, g.ldx) || !fits(trans_b ? g.n : g.k, g.ldw))
             return MOEGG_ESHAPE;
         any |= g.m > 0;
@@ -382,14 +408,16 @@ moegg_status moegg_grouped_gemm_groups(const moegg_group *groups, int32_t num_gr
     int cus = 0;
     if (device_cus(&cus) != 0)
         return MOEGG_EHIP;
-    return from_hip(moegg::groups_launch(p, trans_b, cus, static_cast<hipStream_t>(stream)));
+    return from_hip(tiled ? moegg::groups_launch(p, trans_b, cus, static_cast<hipStream_t>(stream))
+                          : moegg::groups_any_launch(p, trans_b, cus,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 // Shared checks of the combine entry points.
 static moegg_status check_combine(int64_t num_tokens, int32_t topk, int32_t N, int64_t y_rows,
                                   const int32_t *scatter)
 {
-    if (num_tokens < 0 || topk < 1 || N < 1 || N % 8 != 0 || y_rows < 0)
+    if (num_tokens < 0 || topk < 1 || N < 1 || y_rows < 0)
         return MOEGG_ESHAPE;
     if (num_tokens * topk > INT32_MAX)
         return MOEGG_ESHAPE;
@@ -411,8 +439,11 @@ moegg_status moegg_combine(const void *Y, const int32_t *scatter_idx, const floa
         return MOEGG_EINVAL;
     if (num_tokens == 0)
         return MOEGG_OK;
-    if (!Y || !out || !aligned16(Y) || !aligned16(out))
+    if (!Y || !out || !aligned2(Y) || !aligned2(out))
         return MOEGG_EINVAL;
+    if ((flags & MOEGG_COMBINE_FP32_OUT) && !aligned4(out))
+        return MOEGG_EINVAL;
+    const bool tiled = N % 8 == 0 && aligned16(Y) && aligned16(out);
     moegg::CombineParams p;
     p.Y = static_cast<const char *>(Y);
     p.scatter = scatter_idx;
@@ -424,7 +455,8 @@ moegg_status moegg_combine(const void *Y, const int32_t *scatter_idx, const floa
     p.topk = topk;
     p.N = N;
     p.f32_out = flags & MOEGG_COMBINE_FP32_OUT;
-    return from_hip(moegg::combine_launch(p, static_cast<hipStream_t>(stream)));
+    return from_hip(tiled ? moegg::combine_launch(p, static_cast<hipStream_t>(stream))
+                          : moegg::combine_any_launch(p, static_cast<hipStream_t>(stream)));
 }
 
 moegg_status moegg_combine_bwd(const void *dOut, const void *Y, const int32_t *scatter_idx,
@@ -437,10 +469,11 @@ moegg_status moegg_combine_bwd(const void *dOut, const void *Y, const int32_t *s
         return st;
     if (num_tokens == 0)
         return MOEGG_OK;
-    if (!dOut || !dY || !aligned16(dOut) || !aligned16(dY))
+    if (!dOut || !dY || !aligned2(dOut) || !aligned2(dY))
         return MOEGG_EINVAL;
-    if (dw && (!Y || !aligned16(Y)))
+    if (dw && (!Y || !aligned2(Y)))
         return MOEGG_EINVAL;  // the weight gradient reads the forward input
+    const bool tiled = N % 8 == 0 && aligned16(dOut) && aligned16(dY) && (!dw || aligned16(Y));
     moegg::CombineBwdParams p;
     p.dOut = static_cast<const char *>(dOut);
     p.Y = static_cast<const char *>(Y);
@@ -453,7 +486,8 @@ moegg_status moegg_combine_bwd(const void *dOut, const void *Y, const int32_t *s
     p.y_rows = y_rows;
     p.topk = topk;
     p.N = N;
-    return from_hip(moegg::combine_bwd_launch(p, static_cast<hipStream_t>(stream)));
+    return from_hip(tiled ? moegg::combine_bwd_launch(p, static_cast<hipStream_t>(stream))
+                          : moegg::combine_bwd_any_launch(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -178,6 +178,93 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdParams a)
     }
 }
 
+// Any N and 2-byte-aligned rows (rows that are not whole 16-byte chunks):
+// the same sums, one column per lane and step, loaded and stored as 2-byte
+// elements.  Not tuned: the tiled kernels above take every N that is a
+// multiple of 8 with 16-byte aligned operands.
+__device__ __forceinline__ float bf16_at(const char *base, int64_t elem)
+{
+    const uint32_t h = *reinterpret_cast<const uint16_t *>(base + elem * 2);
+    return __builtin_bit_cast(float, h << 16);
+}
+
+__global__ __launch_bounds__(256) void combine_fwd_any_kernel(CombineParams a)
+{
+    const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (t >= a.T)
+        return;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int c0 = 0; c0 < a.N; c0 += kWave) {
+        const int col = c0 + lane;
+        float acc = 0.0f;
+        for (int j = 0; j < a.topk; ++j) {
+            const int64_t s = t * a.topk + j;
+            const int64_t row = combine_row(a, s);
+            if (row >= 0 && col < a.N)
+                acc += (a.weights ? a.weights[s] : 1.0f) * bf16_at(a.Y, row * a.N + col);
+        }
+        if (col >= a.N)
+            continue;
+        if (a.f32_out)
+            reinterpret_cast<float *>(a.out)[t * a.N + col] = acc;
+        else
+            *reinterpret_cast<uint16_t *>(a.out + (t * a.N + col) * 2) = to_bf16(acc);
+    }
+}
+
+__global__ __launch_bounds__(256) void combine_bwd_any_kernel(CombineBwdParams a)
+{
+    const int64_t s = (int64_t)blockIdx.x * (blockDim.x / kWave) +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (s >= a.T * a.topk)
+        return;
+    const int64_t t = s / a.topk;
+    int64_t row = s;
+    if (a.scatter) {
+        row = a.scatter[s];
+        if (row >= a.y_rows) {
+            raise_error(a.err, kErrGather);
+            row = -1;
+        }
+    }
+    const float w = a.weights ? a.weights[s] : 1.0f;
+    const int lane = threadIdx.x & (kWave - 1);
+    float dot = 0.0f;
+    if (row >= 0) {
+        for (int col = lane; col < a.N; col += kWave) {
+            const float g = bf16_at(a.dOut, t * a.N + col);
+            if (a.dw)
+                dot += g * bf16_at(a.Y, row * a.N + col);
+            *reinterpret_cast<uint16_t *>(a.dY + (row * a.N + col) * 2) = to_bf16(w * g);
+        }
+    }
+    if (a.dw) {
+        dot = wave_sum(dot);
+        if (lane == 0)
+            a.dw[s] = dot;
+    }
+}
+
+hipError_t combine_any_launch(const CombineParams &p, hipStream_t stream)
+{
+    if (p.T == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(combine_fwd_any_kernel, dim3((unsigned)((p.T + 3) / 4)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+hipError_t combine_bwd_any_launch(const CombineBwdParams &p, hipStream_t stream)
+{
+    const int64_t items = p.T * p.topk;
+    if (items == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(combine_bwd_any_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
 hipError_t combine_launch(const CombineParams &p, hipStream_t stream)
 {
     if (p.T == 0)

@@ -1182,40 +1182,6 @@ __device__ __forceinline__ void epilogue_gated(char *st0, const f32x16_t (&acc)[
 // Expert tables shared by the routed kernels
 // ---------------------------------------------------------------------------
 
-// s_roff[0..E]: expert row starts clipped to [0, S] (s_roff[E] = end);
-// s_tstart[0..E]: first tile of each expert for tiles_of(rows).  Flags
-// negative m_sizes and sums past S.
-template <class TilesOf>
-__device__ __forceinline__ int build_expert_tables(const int32_t *m_sizes, int E, int64_t S,
-                                                   int *s_roff, int *s_tstart, int *s_scratch,
-                                                   int32_t *err, TilesOf tiles_of)
-{
-    bool bad = false;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        const int m = m_sizes[e];
-        bad |= m < 0;
-        s_roff[e] = m < 0 ? 0 : m;
-    }
-    wave0_exclusive_scan(s_roff, E, &s_scratch[0]);
-    const int total = s_scratch[0];
-    if (threadIdx.x == 0) {
-        bad |= total > S || total < 0;
-        s_roff[E] = (int)min((int64_t)total, S);
-    }
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        s_roff[e] = (int)min((int64_t)s_roff[e], S);
-    if (bad)
-        raise_error(err, kErrMSizes);
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-        s_tstart[e] = tiles_of(s_roff[e + 1] - s_roff[e]);
-    wave0_exclusive_scan(s_tstart, E, &s_scratch[1]);
-    if (threadIdx.x == 0)
-        s_tstart[E] = s_scratch[1];
-    __syncthreads();
-    return s_tstart[E];
-}
-
 __device__ __forceinline__ int checked_gather(const int32_t *gather, int64_t p, int64_t S,
                                               int32_t *err)
 {

@@ -152,8 +152,19 @@ __host__ __device__ inline int64_t dw_header_bytes(int E)
 }
 hipError_t groups_launch(const GroupsParams &p, int trans_b, int cus, hipStream_t stream);
 
+// Any-shape path (any K, N, leading dimensions; operands 2-byte aligned):
+// the same results as the launches above, for sizes whose rows cannot be
+// moved as 16-byte chunks.  No workspace.
+hipError_t fwd_any_launch(const FwdParams &p, int cus, hipStream_t stream);
+hipError_t dx_any_launch(const DxParams &p, int cus, hipStream_t stream);
+hipError_t dw_any_launch(const DwParams &p, int cus, hipStream_t stream);
+hipError_t groups_any_launch(const GroupsParams &p, int trans_b, int cus, hipStream_t stream);
+
 hipError_t combine_launch(const CombineParams &p, hipStream_t stream);
 hipError_t combine_bwd_launch(const CombineBwdParams &p, hipStream_t stream);
+// Any N, rows 2-byte aligned (not whole 16-byte chunks).
+hipError_t combine_any_launch(const CombineParams &p, hipStream_t stream);
+hipError_t combine_bwd_any_launch(const CombineBwdParams &p, hipStream_t stream);
 
 int64_t route_chunks(int64_t S);
 hipError_t route_scratch(int32_t **out);

@@ -65,13 +65,7 @@ __device__ __forceinline__ int64_t combine_row(const CombineParams &a, int64_t s
 // before summing.  Each of the token's rows is thus read front to back by one
 // wave, in 1 KiB pieces close together in time, which HBM serves better than
 // the same pieces spread over several waves.
-#ifndef MOEGG_COMBINE_CPI
-#define MOEGG_COMBINE_CPI 4
-#endif
-constexpr int kCombineCpi = MOEGG_COMBINE_CPI;
-#ifndef MOEGG_COMBINE_BWD_UNROLL
-#define MOEGG_COMBINE_BWD_UNROLL 4
-#endif
+constexpr int kCombineCpi = 4;
 
 __global__ __launch_bounds__(256) void combine_fwd_kernel(CombineParams a)
 {
@@ -153,7 +147,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(CombineBwdParams a)
     const int lane = threadIdx.x & (kWave - 1);
     float dot = 0.0f;
     if (row >= 0) {
-#pragma unroll MOEGG_COMBINE_BWD_UNROLL
+#pragma unroll 4
         for (int c0 = 0; c0 < a.N; c0 += kChunk) {
             const int col = c0 + lane * 8;
             if (col >= a.N)

@@ -1961,23 +1961,11 @@ __global__ __launch_bounds__(C::NT) void groups_kernel(GroupsParams a)
 // ---------------------------------------------------------------------------
 
 // Tile shapes: <BM, BN, waves along M, waves along N>.
-#ifndef MOEGG_FWD_CFG
-#define MOEGG_FWD_CFG 256, 256, 2, 4
-#endif
-#ifndef MOEGG_DX_CFG
-#define MOEGG_DX_CFG 256, 256, 2, 4
-#endif
-#ifndef MOEGG_DW_CFG
-#define MOEGG_DW_CFG 256, 256, 2, 4
-#endif
-#ifndef MOEGG_SMALL_CFG
-#define MOEGG_SMALL_CFG 32, 128, 1, 4
-#endif
-using BigCfg = Cfg<MOEGG_FWD_CFG>;       // many rows per expert
-using DxCfg = Cfg<MOEGG_DX_CFG>;
+using BigCfg = Cfg<256, 256, 2, 4>;     // many rows per expert
+using DxCfg = Cfg<256, 256, 2, 4>;
 using DxQuadCfg = Cfg<256, 256, 2, 2>;  // long reductions: four-wave engine
-using DwCfg = Cfg<MOEGG_DW_CFG>;
-using SmallCfg = Cfg<MOEGG_SMALL_CFG>;   // few rows per expert: stream the weights
+using DwCfg = Cfg<256, 256, 2, 4>;
+using SmallCfg = Cfg<32, 128, 1, 4>;    // few rows per expert: stream the weights
 using DxSmallCfg = Cfg<32, 128, 1, 4>;     // the same for dX
 using SmallGatedCfg = Cfg<32, 256, 1, 4>;  // the same with two blocks per wave to pair
 // Small explicit groups: tiles of 64 x 128 so that the dual-expert layer's
@@ -2259,9 +2247,7 @@ constexpr int kDxQuadMinN = 8192;
 // weights are then streamed once per 32-row tile (a decode slice), where
 // 256 x 256 tiles would leave about one long, latency-bound tile per CU
 // (T=64 top-8 of E=128, N=2048, K=768: 0.064 ms against 0.114 ms).
-#ifndef MOEGG_SMALL_ROWS
-#define MOEGG_SMALL_ROWS 96
-#endif
+constexpr int64_t kSmallRows = 96;
 
 // Workspace of the tail split: the header and at most G partials of one
 // tile (R * P <= G), for the grid the launch below will use.
@@ -2277,7 +2263,7 @@ static int64_t dx_ws_cfg(int cus)
 int64_t dx_workspace_bytes(int64_t S, int E, int N, int K, int cus)
 {
     (void)K;
-    if (S / E < MOEGG_SMALL_ROWS)
+    if (S / E < kSmallRows)
         return 0;
     if (N >= kDxQuadMinN)
         return dx_ws_cfg<DxQuadCfg>(cus);
@@ -2286,7 +2272,7 @@ int64_t dx_workspace_bytes(int64_t S, int E, int N, int K, int cus)
 
 hipError_t dx_launch(const DxParams &p, int cus, hipStream_t stream)
 {
-    if (p.S / p.E < MOEGG_SMALL_ROWS)
+    if (p.S / p.E < kSmallRows)
         dx_launch_cfg<DxSmallCfg>(p, cus, stream);
     else if (p.N >= kDxQuadMinN)
         dx_launch_cfg<DxQuadCfg>(p, cus, stream);

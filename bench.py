@@ -237,12 +237,22 @@ WORKLOAD_DESC = {
 }
 
 
-def time_step(st, steps, warmup):
+def time_step(st, steps, warmup, min_warm_s=0.0):
+    """Run `warmup` untimed steps (then more, doubling, until min_warm_s
+    seconds have passed), then time `steps` steps with HIP events on the
+    launch stream: per-kernel ms, step ms and wall seconds."""
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        for _, fn, _, _ in st.kernels:
-            fn()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    batch, done = warmup, 0
+    while batch > 0:
+        for _ in range(batch):
+            for _, fn, _, _ in st.kernels:
+                fn()
+        done += batch
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_warm_s:
+            break
+        batch = done
     nk = len(st.kernels)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -707,6 +717,10 @@ def kernel_breakdown(st, per):
     return out
 
 
+# MI355X raises its clock over the first tens of milliseconds of load, so the
+# short configurations warm up for at least this long.
+CONFIG_MIN_WARMUP_S = 0.1
+
 # Every configuration of the benchmark besides the headline one, timed in the
 # default run: (key, workload, kernels reported, steps, warmup).
 CONFIG_RUNS = (
@@ -725,7 +739,7 @@ def run_configs():
     for key, workload, labels, steps, warmup in CONFIG_RUNS:
         print(f"config {key} ({workload})", file=sys.stderr, flush=True)
         st = make_step(workload)
-        per, step_ms, _ = time_step(st, steps, warmup)
+        per, step_ms, _ = time_step(st, steps, warmup, min_warm_s=CONFIG_MIN_WARMUP_S)
         bd = kernel_breakdown(st, per)
         out[key] = {"workload": workload, "desc": WORKLOAD_DESC[workload], "steps": steps,
                     "step_ms": round(step_ms, 4),

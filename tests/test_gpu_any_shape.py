@@ -217,3 +217,29 @@ def test_combine_any_n(mg, case):
     absdot = np.array([np.sum(np.abs(Gw[s // topk]) * np.abs(Yw[sc[s]])) for s in range(T * topk)])
     err = np.abs(dw.cpu().numpy().astype(np.float64) - dw_ref)
     assert np.all(err <= 2 * gamma(N) * (absdot + np.abs(dw_ref)) + 1e-30)
+
+
+def test_any_shape_many_blocks(mg):
+    """A mid-size odd shape (many 32 x 32 blocks per expert and many waves
+    per workgroup loop): T 1024, top-2 over 8 experts, K 1000, N 1001, on
+    sampled rows against the oracle."""
+    wl = synth.random_case(1024, 1000, 1001, 8, 2, PX, 59, empty=(5,), with_dy=True)
+    r, ref_route = _routes(mg, wl)
+    E, N, K = wl.W.shape
+    rows = np.unique(np.concatenate([np.arange(0, wl.S, 97), [wl.S - 1]]))
+    Y = mg.grouped_gemm_fwd(_dev(wl.X), _dev(wl.W), r["m_sizes"], r["gather"], None, wl.topk, PX)
+    dX = mg.grouped_gemm_dX(_dev(wl.dY), _dev(wl.W), r["m_sizes"], r["gather"], wl.topk, PX)
+    dW = mg.grouped_gemm_dW(_dev(wl.X), _dev(wl.dY), r["m_sizes"], r["gather"], wl.topk, PX)
+    torch.cuda.synchronize()
+    rr, rg = ref_route["m_sizes"], ref_route["gather"]
+    sel = torch.as_tensor(rows, dtype=torch.long, device="cuda")
+    _check(Y[sel], oracle.grouped_gemm_fwd(synth.bits(wl.X), synth.bits(wl.W), rr, rg, None,
+                                          wl.topk, PX, rows=rows), "fwd 1024x1000x1001")
+    _check(dX[sel], oracle.grouped_gemm_dX(synth.bits(wl.dY), synth.bits(wl.W), rr, rg, wl.topk,
+                                          PX, rows=rows), "dX 1024x1000x1001")
+    wrows = np.unique(np.concatenate([np.arange(0, E * N, 131), [E * N - 1]]))
+    wsel = torch.as_tensor(wrows, dtype=torch.long, device="cuda")
+    _check(dW.reshape(E * N, K)[wsel], oracle.grouped_gemm_dW(
+        synth.bits(wl.X), synth.bits(wl.dY), rr, rg, wl.topk, PX, E, rows=wrows),
+        "dW 1024x1000x1001")
+    assert torch.count_nonzero(dW[5]).item() == 0
